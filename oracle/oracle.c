@@ -1,0 +1,405 @@
+/*
+ * oracle.c -- plain, slow, single-threaded CPU reference for the MoE token
+ * dispatch/combine path.
+ *
+ * TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load or call this library.  The HIP
+ * library never links it and shares no source with it.
+ *
+ * Every function is a direct loop over the definition of the operation.
+ * Sources (page titles; the section or table named):
+ *   [EPA] "DeepEP-Ascend" README -- "API Overview" table
+ *         (get_dispatch_layout / dispatch / combine / low_latency_*),
+ *         "Environment Variables" table (MOE_EXPERT_TOKEN_NUMS_TYPE:
+ *         count vs prefix sum; MOE_ENABLE_TOPK_NEG_ONE: -1 = not
+ *         dispatched), "Quantization Modes in Normal Dispatch" table
+ *         (float8_e4m3fn payload with float32 scales).
+ *   [ECR] "[Feature Request] Support Expert-Choice Routing via Native
+ *         Expert-Centric API ([num_experts, capacity])" -- "Proposed
+ *         Solutions", Solution 1 (token_indices [num_experts, capacity]
+ *         int32 plus expert weights).
+ * Where the pages leave a step open (index dtype, row order inside an
+ * expert, capacity overflow, the 128-channel fp8 group and scale rule,
+ * accumulation precision), the reading taken is stated at the function.
+ *
+ * Floating point: built with -O2 -ffp-contract=off, no fast-math, SSE
+ * arithmetic (no excess precision).  fp32 is used exactly where the method
+ * fixes it (the fp8 scale and the value that is rounded to e4m3); sums are
+ * accumulated in fp64 and rounded once.
+ *
+ * Parity pins (tests/test_oracle_*.py): numpy brute force on tiny inputs,
+ * hand-derived fixtures in tests/golden/, closed forms (unit-weight round
+ * trip = bf16(multiplicity * x), the amax element encodes to +-448), the
+ * e4m3 converter against a nearest-code search and against torch's
+ * float8_e4m3fn cast, and the bf16 rounding against torch's cast.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* Number formats                                                      */
+/* ------------------------------------------------------------------ */
+
+/* bf16 bits -> fp32: the bf16 pattern is the top half of an fp32 pattern. */
+float oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round a real number (given as fp64) to the nearest bf16 value, ties to
+ * the even significand, and return its bit pattern.  bf16 keeps 8
+ * significant bits and fp32's exponent range; below 2^-126 the spacing is
+ * the subnormal quantum 2^-133.  Overflow gives infinity (never reached by
+ * in-contract inputs; NaN input is out of contract). */
+uint16_t oracle_bf16_from_f64(double v)
+{
+    if (v == 0.0)
+        return signbit(v) ? 0x8000u : 0x0000u;
+    double a = fabs(v);
+    int e;
+    frexp(a, &e);            /* a in [2^(e-1), 2^e) */
+    int ex = e - 1;          /* floor(log2(a)) */
+    int qexp = (ex < -126) ? -133 : ex - 7;
+    double q = nearbyint(ldexp(a, -qexp));   /* exact scaling, then RNE */
+    double r = ldexp(q, qexp);
+    float f = (float)r;      /* exact: r is a bf16 value (or overflows to inf) */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t h = (uint16_t)(u >> 16);
+    return signbit(v) ? (uint16_t)(h | 0x8000u) : h;
+}
+
+/* fp32 -> OCP 8-bit E4M3 ("float8_e4m3fn") code, round to nearest, ties to
+ * the even code.  E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits; no infinities; S.1111.111 is NaN, so the largest finite magnitude is
+ * 1.75 * 2^8 = 448; subnormals are m * 2^-9, m = 1..7.
+ * Magnitudes >= 464 (the midpoint above 448) saturate to 448 (readings: the
+ * format has no infinity, and in-contract inputs never exceed 448*(1+2^-23),
+ * which rounds to 448 anyway).  The sign of zero is kept. */
+uint8_t oracle_e4m3_from_f32(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80u : 0x00u;
+    double a = fabs((double)v);              /* exact */
+    if (a >= 464.0)
+        return (uint8_t)(sign | 0x7Eu);
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);
+    int ex = e - 1;                          /* floor(log2(a)) */
+    int qexp = (ex < -6) ? -9 : ex - 3;      /* 4 significant bits, or the subnormal quantum */
+    double q = nearbyint(ldexp(a, -qexp));   /* RNE to an integer multiple of 2^qexp */
+    double r = ldexp(q, qexp);               /* the chosen e4m3 value */
+    if (r == 0.0)
+        return sign;
+    frexp(r, &e);
+    ex = e - 1;                              /* may have carried into the next binade */
+    if (ex < -6)                             /* subnormal: r = m * 2^-9 */
+        return (uint8_t)(sign | (uint8_t)ldexp(r, 9));
+    int m = (int)ldexp(r, 3 - ex) - 8;       /* r = (8 + m) * 2^(ex-3) */
+    return (uint8_t)(sign | (uint8_t)(((ex + 7) << 3) | m));
+}
+
+/* Value of an E4M3 code (NaN codes return NaN). */
+float oracle_e4m3_to_f32(uint8_t c)
+{
+    int s = (c >> 7) & 1, ef = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (ef == 15 && m == 7)
+        return NAN;
+    if (ef == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(8.0 + m, ef - 7 - 3);
+    return (float)(s ? -v : v);
+}
+
+/* Array forms, for tests. */
+void oracle_e4m3_from_f32_array(const float *in, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e4m3_from_f32(in[i]);
+}
+
+void oracle_bf16_from_f64_array(const double *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_from_f64(in[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Token choice                                                        */
+/* ------------------------------------------------------------------ */
+
+/* Dispatch layout ([EPA] API Overview, get_dispatch_layout; Environment
+ * Variables, MOE_EXPERT_TOKEN_NUMS_TYPE and MOE_ENABLE_TOPK_NEG_ONE).
+ *   topk_idx [T,K] int32.  -1 = padding (not dispatched).  Any other value
+ *   outside [0,E) is invalid: counted in num_invalid and treated like -1.
+ *   counts[e]   = number of valid (t,k) with topk_idx[t,k] == e   (count form)
+ *   offsets[e]  = sum of counts[0..e-1], offsets[E] = N           (prefix form)
+ *   Experts are split into R equal contiguous blocks (rank r owns experts
+ *   [r*E/R, (r+1)*E/R)); is_token_in_rank[t,r] = 1 when token t has at least
+ *   one valid slot on rank r; tokens_per_rank[r] = sum over t of that.
+ * tokens_per_rank / is_token_in_rank may be NULL. */
+void oracle_layout(const int32_t *topk_idx, int T, int K, int E, int R,
+                   int32_t *counts, int32_t *offsets, int32_t *tokens_per_rank,
+                   uint8_t *is_token_in_rank, int32_t *num_invalid)
+{
+    int per_rank = E / R;
+    uint8_t *row = (uint8_t *)calloc((size_t)R, 1);
+    for (int e = 0; e < E; ++e)
+        counts[e] = 0;
+    if (tokens_per_rank)
+        for (int r = 0; r < R; ++r)
+            tokens_per_rank[r] = 0;
+    *num_invalid = 0;
+    for (int t = 0; t < T; ++t) {
+        memset(row, 0, (size_t)R);
+        for (int k = 0; k < K; ++k) {
+            int32_t e = topk_idx[(int64_t)t * K + k];
+            if (e == -1)
+                continue;
+            if (e < 0 || e >= E) {
+                (*num_invalid)++;
+                continue;
+            }
+            counts[e]++;
+            row[e / per_rank] = 1;
+        }
+        for (int r = 0; r < R; ++r) {
+            if (is_token_in_rank)
+                is_token_in_rank[(int64_t)t * R + r] = row[r];
+            if (tokens_per_rank)
+                tokens_per_rank[r] += row[r];
+        }
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+    free(row);
+}
+
+/* Slot assignment: the receive row of every (t,k) ([EPA] API Overview,
+ * dispatch returns the handle that combine must use; low_latency_dispatch
+ * takes a per-expert capacity, num_max_dispatch_tokens_per_rank).
+ * Readings: rows of one expert are in ascending (t,k) order (a stable
+ * scatter), experts in ascending order.  With r = number of earlier valid
+ * (t',k') < (t,k) that chose the same expert e:
+ *   contiguous (padded == 0): slot = offsets[e] + r, kept only if
+ *       slot < max_rows (the receive buffer's row count);
+ *   padded (padded != 0):     slot = e*cap + r, kept only if r < cap.
+ * A slot that is not kept is -1 and counts in num_dropped; padding and
+ * invalid entries get -1 and are not counted.  recv_src[slot] = t. */
+void oracle_slots(const int32_t *topk_idx, int T, int K, int E, int padded,
+                  int cap_or_max_rows, int32_t *slot, int32_t *recv_src,
+                  int32_t *num_dropped)
+{
+    int32_t *counts = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    int32_t *offsets = (int32_t *)calloc((size_t)E + 1, sizeof(int32_t));
+    int32_t *cursor = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    int32_t inval;
+    oracle_layout(topk_idx, T, K, E, 1, counts, offsets, NULL, NULL, &inval);
+    *num_dropped = 0;
+    for (int t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            int64_t i = (int64_t)t * K + k;
+            int32_t e = topk_idx[i];
+            if (e < 0 || e >= E) {
+                slot[i] = -1;
+                continue;
+            }
+            int r = cursor[e]++;
+            int64_t s;
+            if (padded)
+                s = (r < cap_or_max_rows) ? (int64_t)e * cap_or_max_rows + r : -1;
+            else
+                s = ((int64_t)offsets[e] + r < cap_or_max_rows) ? (int64_t)offsets[e] + r : -1;
+            if (s < 0) {
+                (*num_dropped)++;
+                slot[i] = -1;
+                continue;
+            }
+            slot[i] = (int32_t)s;
+            if (recv_src)
+                recv_src[s] = t;
+        }
+    }
+    free(counts);
+    free(offsets);
+    free(cursor);
+}
+
+/* bf16 dispatch ([EPA] API Overview, dispatch; Quantization Modes, "bf16"):
+ * recv[slot[t,k], :] = x[t, :] for every kept slot.  A byte copy. */
+void oracle_dispatch_bf16(const uint16_t *x, int T, int H, const int32_t *slot, int K,
+                          uint16_t *recv)
+{
+    for (int t = 0; t < T; ++t)
+        for (int k = 0; k < K; ++k) {
+            int32_t s = slot[(int64_t)t * K + k];
+            if (s < 0)
+                continue;
+            memcpy(recv + (int64_t)s * H, x + (int64_t)t * H, (size_t)H * sizeof(uint16_t));
+        }
+}
+
+/* fp8 dispatch ([EPA] Quantization Modes: float8_e4m3fn payload with float32
+ * scales).  The 128-channel group and its scale rule are not on the pages
+ * (they list per-token and per-32 granularity); the rule taken is:
+ * per token t and group g (channels 128g .. 128g+127)
+ *   a = max |x|                 (exact)
+ *   a == 0: s = 0 and every code is 0x00
+ *   else:   s = a / 448         (fp32 division, round to nearest even)
+ *           q_i = e4m3(x_i / s) (fp32 division, then the RNE encoder above)
+ * and q, s are written to every kept slot of t: recv_q [rows, H] codes,
+ * recv_s [rows, H/128] fp32. */
+void oracle_dispatch_fp8(const uint16_t *x, int T, int H, const int32_t *slot, int K,
+                         uint8_t *recv_q, float *recv_s)
+{
+    int G = H / 128;
+    uint8_t *q = (uint8_t *)malloc((size_t)H + 1);
+    float *s = (float *)malloc(((size_t)G + 1) * sizeof(float));
+    for (int t = 0; t < T; ++t) {
+        const uint16_t *xr = x + (int64_t)t * H;
+        for (int g = 0; g < G; ++g) {
+            float a = 0.0f;
+            for (int i = 0; i < 128; ++i) {
+                float v = fabsf(oracle_bf16_to_f32(xr[128 * g + i]));
+                if (v > a)
+                    a = v;
+            }
+            if (a == 0.0f) {
+                s[g] = 0.0f;
+                for (int i = 0; i < 128; ++i)
+                    q[128 * g + i] = 0x00;
+                continue;
+            }
+            float sg = a / 448.0f;
+            s[g] = sg;
+            for (int i = 0; i < 128; ++i) {
+                float v = oracle_bf16_to_f32(xr[128 * g + i]);
+                q[128 * g + i] = oracle_e4m3_from_f32(v / sg);
+            }
+        }
+        for (int k = 0; k < K; ++k) {
+            int32_t sl = slot[(int64_t)t * K + k];
+            if (sl < 0)
+                continue;
+            memcpy(recv_q + (int64_t)sl * H, q, (size_t)H);
+            memcpy(recv_s + (int64_t)sl * G, s, (size_t)G * sizeof(float));
+        }
+    }
+    free(q);
+    free(s);
+}
+
+/* Combine ([EPA] API Overview: combine reduces the dispatched rows through
+ * the handle; low_latency_combine also takes topk_weights):
+ *   out[t, h] = bf16( sum over k with slot >= 0 of w[t,k] * y[slot[t,k], h] )
+ * w == NULL means unit weights (the plain normal-mode sum).  The sum is the
+ * exact real sum up to fp64 rounding (products of an fp32 weight and a bf16
+ * value are exact in fp64), rounded once to bf16.  A token with no kept slot
+ * gives +0. */
+void oracle_combine(const uint16_t *y, int H, const int32_t *slot, const float *w,
+                    int T, int K, uint16_t *out)
+{
+    double *acc = (double *)malloc(((size_t)H + 1) * sizeof(double));
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h)
+            acc[h] = 0.0;
+        for (int k = 0; k < K; ++k) {
+            int32_t s = slot[(int64_t)t * K + k];
+            if (s < 0)
+                continue;
+            double wk = w ? (double)w[(int64_t)t * K + k] : 1.0;
+            const uint16_t *yr = y + (int64_t)s * H;
+            for (int h = 0; h < H; ++h)
+                acc[h] += wk * (double)oracle_bf16_to_f32(yr[h]);
+        }
+        for (int h = 0; h < H; ++h)
+            out[(int64_t)t * H + h] = oracle_bf16_from_f64(acc[h]);
+    }
+    free(acc);
+}
+
+/* ------------------------------------------------------------------ */
+/* Expert choice ([ECR] Solution 1)                                    */
+/* ------------------------------------------------------------------ */
+
+/* recv[e, c, :] = x[token_indices[e, c], :].  Entries equal to -1 are empty
+ * and leave their row untouched; other values outside [0,T) are invalid:
+ * counted and skipped (reading).  Duplicates are allowed. */
+void oracle_ec_dispatch(const uint16_t *x, int T, int H, const int32_t *token_indices,
+                        int E, int C, uint16_t *recv, int32_t *num_invalid)
+{
+    *num_invalid = 0;
+    for (int64_t j = 0; j < (int64_t)E * C; ++j) {
+        int32_t i = token_indices[j];
+        if (i == -1)
+            continue;
+        if (i < 0 || i >= T) {
+            (*num_invalid)++;
+            continue;
+        }
+        memcpy(recv + j * H, x + (int64_t)i * H, (size_t)H * sizeof(uint16_t));
+    }
+}
+
+/* Token -> entries map (the inverse of token_indices, kept as the handle for
+ * combine): for token t the flat entries j = e*C + c with
+ * token_indices[j] == t, ascending in j, stored in
+ * tok_ent[tok_off[t] .. tok_off[t+1]); tok_off[T] = number of valid entries. */
+void oracle_ec_invert(const int32_t *token_indices, int E, int C, int T,
+                      int32_t *tok_off, int32_t *tok_ent)
+{
+    int64_t n = (int64_t)E * C;
+    int32_t *cursor = (int32_t *)calloc((size_t)T + 1, sizeof(int32_t));
+    for (int t = 0; t <= T; ++t)
+        tok_off[t] = 0;
+    for (int64_t j = 0; j < n; ++j) {
+        int32_t i = token_indices[j];
+        if (i >= 0 && i < T)
+            tok_off[i + 1]++;
+    }
+    for (int t = 0; t < T; ++t)
+        tok_off[t + 1] += tok_off[t];
+    for (int64_t j = 0; j < n; ++j) {
+        int32_t i = token_indices[j];
+        if (i >= 0 && i < T)
+            tok_ent[tok_off[i] + cursor[i]++] = (int32_t)j;
+    }
+    free(cursor);
+}
+
+/* out[t, h] = bf16( sum over j with token_indices[j] == t, j ascending, of
+ * w[j] * y[j, h] ) with y [E*C, H]; tokens that no expert chose give +0.
+ * Accumulation as in oracle_combine.  Only tokens in `tokens` (n_tokens of
+ * them; NULL = all T in order) are computed, into consecutive rows of out. */
+void oracle_ec_combine(const uint16_t *y, const float *w, const int32_t *token_indices,
+                       int E, int C, int H, int T, const int32_t *tokens, int n_tokens,
+                       uint16_t *out)
+{
+    int64_t n = (int64_t)E * C;
+    int count = tokens ? n_tokens : T;
+    double *acc = (double *)malloc(((size_t)H + 1) * sizeof(double));
+    for (int o = 0; o < count; ++o) {
+        int t = tokens ? tokens[o] : o;
+        for (int h = 0; h < H; ++h)
+            acc[h] = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            if (token_indices[j] != t)
+                continue;
+            const uint16_t *yr = y + j * H;
+            for (int h = 0; h < H; ++h)
+                acc[h] += (double)w[j] * (double)oracle_bf16_to_f32(yr[h]);
+        }
+        for (int h = 0; h < H; ++h)
+            out[(int64_t)o * H + h] = oracle_bf16_from_f64(acc[h]);
+    }
+    free(acc);
+}

@@ -1,0 +1,164 @@
+"""Deliberately naive numpy/Python brute force, independent of oracle/.
+
+Each function restates a definition in the most direct way available (sorting
+tuples, nearest-value search, per-element loops) so that a mistake in the C
+oracle shows up as a disagreement.  Tiny inputs only.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def layout(topk_idx, E, R=1):
+    T, K = topk_idx.shape
+    valid = (topk_idx >= 0) & (topk_idx < E)
+    counts = np.bincount(topk_idx[valid].astype(np.int64), minlength=E).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    itr = np.zeros((T, R), np.uint8)
+    per = E // R
+    for t in range(T):
+        for k in range(K):
+            if valid[t, k]:
+                itr[t, topk_idx[t, k] // per] = 1
+    tpr = itr.sum(axis=0).astype(np.int32)
+    ninv = int(((topk_idx != -1) & ~valid).sum())
+    return dict(counts=counts, offsets=offsets, tokens_per_rank=tpr,
+                is_token_in_rank=itr, num_invalid=ninv)
+
+
+def slots(topk_idx, E, padded, cap_or_max_rows):
+    """Sort the (e, t, k) tuples of valid entries; the position of a tuple in
+    that order is its contiguous row; its position inside its expert is its
+    rank r."""
+    T, K = topk_idx.shape
+    tuples = sorted((int(topk_idx[t, k]), t, k) for t in range(T) for k in range(K)
+                    if 0 <= topk_idx[t, k] < E)
+    slot = np.full((T, K), -1, np.int32)
+    first = {}
+    dropped = 0
+    for pos, (e, t, k) in enumerate(tuples):
+        first.setdefault(e, pos)
+        r = pos - first[e]
+        if padded:
+            s = e * cap_or_max_rows + r if r < cap_or_max_rows else -1
+        else:
+            s = pos if pos < cap_or_max_rows else -1
+        if s < 0:
+            dropped += 1
+        slot[t, k] = s
+    return slot, dropped
+
+
+# ------------------------------------------------------------- e4m3 / bf16
+def e4m3_table():
+    """Value of every E4M3 code from the bit-field definition: bias 7,
+    3 mantissa bits, exponent field 0 = subnormal, S.1111.111 = NaN."""
+    vals = np.empty(256, np.float64)
+    for c in range(256):
+        s, ef, m = c >> 7, (c >> 3) & 15, c & 7
+        if ef == 15 and m == 7:
+            v = np.nan
+        elif ef == 0:
+            v = m / 8.0 * 2.0 ** (1 - 7)
+        else:
+            v = (1 + m / 8.0) * 2.0 ** (ef - 7)
+        vals[c] = -v if s else v
+    return vals
+
+
+def e4m3_nearest(v):
+    """Nearest finite E4M3 code to each fp32 value (searching all codes of
+    the value's sign), ties to the even code; magnitudes above 448 saturate
+    to 448.  Vectorised brute-force search."""
+    v = np.asarray(v, np.float32).astype(np.float64)
+    tab = e4m3_table()
+    pos_codes = np.array([c for c in range(128) if not np.isnan(tab[c])])   # 0x00..0x7E
+    pos_vals = tab[pos_codes]
+    a = np.minimum(np.abs(v), 448.0 * 2)  # beyond 448 every search returns 448
+    d = np.abs(a[:, None] - pos_vals[None, :])
+    dmin = d.min(axis=1, keepdims=True)
+    cand = d == dmin
+    # among tied candidates prefer the even code
+    even = (pos_codes % 2 == 0)[None, :]
+    pick_even = cand & even
+    has_even = pick_even.any(axis=1)
+    choose = np.where(has_even[:, None], pick_even, cand)
+    code = pos_codes[np.argmax(choose, axis=1)]
+    sign = np.signbit(v)
+    return (code | np.where(sign, 0x80, 0)).astype(np.uint8)
+
+
+def bf16_nearest_f64(v):
+    """Nearest bf16 to a float64 value by listing the two bf16 neighbours
+    (truncation and next-up in fp32 bit space), ties to even."""
+    out = np.empty(len(v), np.uint16)
+    for i, x in enumerate(np.asarray(v, np.float64)):
+        if x == 0:
+            out[i] = 0x8000 if np.signbit(x) else 0
+            continue
+        a = abs(x)
+        # bf16 candidates around a: take the fp32 just below/above, truncate
+        lo_bits = np.array([a], np.float32).view(np.uint32)[0] & 0xFFFF0000
+        lo = float(np.array([lo_bits], np.uint32).view(np.float32)[0])
+        if lo > a:
+            lo_bits -= 0x10000
+            lo = float(np.array([lo_bits], np.uint32).view(np.float32)[0])
+        hi_bits = lo_bits + 0x10000
+        hi = float(np.array([hi_bits], np.uint32).view(np.float32)[0])
+        if a - lo < hi - a:
+            b = lo_bits
+        elif hi - a < a - lo:
+            b = hi_bits
+        else:
+            b = lo_bits if ((lo_bits >> 16) & 1) == 0 else hi_bits
+        b = int(b) >> 16
+        out[i] = b | (0x8000 if x < 0 else 0)
+    return out
+
+
+def bf16_to_f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def fp8_quant_token(xrow_bits):
+    """Per-128-channel e4m3 quantisation of one bf16 row, written with
+    numpy float32 arithmetic and the brute-force encoder."""
+    x = bf16_to_f64(xrow_bits).astype(np.float32)
+    H = x.size
+    q = np.empty(H, np.uint8)
+    s = np.empty(H // 128, np.float32)
+    for g in range(H // 128):
+        blk = x[128 * g:128 * (g + 1)]
+        a = np.float32(np.abs(blk).max())
+        if a == 0:
+            s[g] = 0
+            q[128 * g:128 * (g + 1)] = 0
+            continue
+        sg = np.float32(a / np.float32(448.0))
+        s[g] = sg
+        q[128 * g:128 * (g + 1)] = e4m3_nearest((blk / sg).astype(np.float32))
+    return q, s
+
+
+def combine_f64(y_bits, slot, w):
+    """Per-element loops, fp64 sums, rounded to bf16 by bf16_nearest_f64."""
+    T, K = slot.shape
+    H = y_bits.shape[1]
+    acc = np.zeros((T, H), np.float64)
+    yf = bf16_to_f64(y_bits)
+    for t in range(T):
+        for k in range(K):
+            s = slot[t, k]
+            if s >= 0:
+                acc[t] += (1.0 if w is None else float(w[t, k])) * yf[s]
+    return bf16_nearest_f64(acc.ravel()).reshape(T, H)
+
+
+def ec_invert(token_indices, T):
+    flat = token_indices.reshape(-1)
+    valid = (flat >= 0) & (flat < T)
+    j = np.nonzero(valid)[0]
+    order = np.argsort(flat[j], kind="stable")      # CSR transpose by stable sort
+    ent = j[order].astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(np.bincount(flat[j], minlength=T))]).astype(np.int32)
+    return off, ent

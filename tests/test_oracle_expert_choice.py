@@ -1,0 +1,100 @@
+"""Pins for the oracle's expert-choice path: dispatch, inverse map, combine."""
+import numpy as np
+import pytest
+
+import brute
+import golden_io
+import oracle
+from combine_get_dispatch_04_amd import workloads as W
+
+
+def _fixture():
+    g = golden_io.read_kv("expert_choice_small.txt")
+    E, C, T = g["E"][0], g["C"][0], g["T"][0]
+    ti = np.array(g["token_indices"], np.int32).reshape(E, C)
+    w = np.array(g["weights"], np.float32).reshape(E, C)
+    return g, E, C, T, ti, w
+
+
+def test_golden_inverse_and_combine():
+    g, E, C, T, ti, w = _fixture()
+    off, ent = oracle.ec_invert(ti, T)
+    assert off.tolist() == g["tok_off"]
+    assert ent[:off[-1]].tolist() == g["tok_ent"]
+    H = 8
+    x = W.bf16_bits(np.repeat(np.array(g["x_row_values"], np.float32)[:, None], H, axis=1))
+    recv, ninv = oracle.ec_dispatch(x, ti)
+    assert ninv == g["num_invalid"][0]
+    out = oracle.ec_combine(recv, w, ti, T)
+    assert (out == np.array(g["out_bf16"], np.uint16)[:, None]).all()
+
+
+def test_golden_dispatch_rows():
+    g, E, C, T, ti, w = _fixture()
+    H = 8
+    x = W.bf16_bits(np.repeat(np.array(g["x_row_values"], np.float32)[:, None], H, axis=1))
+    sentinel = np.full((E, C, H), 0xABCD, np.uint16)
+    recv, _ = oracle.ec_dispatch(x, ti, sentinel)
+    for e in range(E):
+        for c in range(C):
+            i = ti[e, c]
+            if 0 <= i < T:
+                assert (recv[e, c] == x[i]).all()
+            else:
+                assert (recv[e, c] == 0xABCD).all()      # empty / invalid rows untouched
+
+
+@pytest.mark.parametrize("seed,T,E,C,hot", [(0, 1, 1, 1, 0), (1, 10, 3, 4, 0), (2, 50, 8, 16, 3),
+                                            (3, 7, 40, 5, 1), (4, 200, 16, 32, 0), (5, 0, 2, 3, 0)])
+def test_invert_vs_stable_argsort(seed, T, E, C, hot):
+    c = W.random_expert_choice(seed, T, 8, E, C, p_empty=0.2, p_invalid=0.1, hot=hot)
+    off, ent = oracle.ec_invert(c.token_indices, T)
+    off2, ent2 = brute.ec_invert(c.token_indices, T)
+    assert np.array_equal(off, off2)
+    assert np.array_equal(ent[:off[-1]], ent2)
+
+
+def test_expert_choice_workload_shape():
+    c = W.expert_choice()
+    ti = c.token_indices
+    assert ti.shape == (64, 256) and ti.min() >= 0 and ti.max() < c.T
+    _, m = np.unique(ti, return_counts=True)
+    assert m.max() == 64 and (m > 32).sum() > 100     # many tokens beyond a 32-expert limit
+    for e in range(c.E):
+        assert len(np.unique(ti[e])) == c.C            # top-C picks distinct tokens
+    assert np.allclose(c.weights.sum(axis=1), 1.0, atol=1e-5)
+
+
+def test_ec_combine_unit_weight_round_trip():
+    """Unit weights with y = dispatch(x): out[t] = bf16(m_t * x_t), m_t = number
+    of entries that picked t (up to 64 here); unpicked tokens -> +0."""
+    c = W.random_expert_choice(8, 120, 32, 48, 20, p_empty=0.1, hot=6)
+    recv, _ = oracle.ec_dispatch(c.x, c.token_indices)
+    out = oracle.ec_combine(recv, np.ones((c.E, c.C), np.float32), c.token_indices, c.T)
+    flat = c.token_indices.ravel()
+    m = np.bincount(flat[flat >= 0], minlength=c.T).astype(np.float32)
+    assert m.max() >= 40
+    ref = W.bf16_bits(W.bf16_to_f32(c.x) * m[:, None])
+    assert np.array_equal(out, ref)
+    assert (out[m == 0] == 0).all()
+
+
+def test_ec_combine_vs_brute_weighted():
+    c = W.random_expert_choice(9, 30, 16, 6, 9, p_empty=0.2, p_invalid=0.1, hot=2)
+    rng = np.random.default_rng(90)
+    y = W.bf16_bits(rng.standard_normal((c.E, c.C, 16), dtype=np.float32))
+    out = oracle.ec_combine(y, c.weights, c.token_indices, c.T)
+    # brute: express the expert-choice sum as a token-choice sum with a slot per entry
+    off, ent = brute.ec_invert(c.token_indices, c.T)
+    K = max(int(np.diff(off).max()), 1)
+    slot = np.full((c.T, K), -1, np.int32)
+    w = np.zeros((c.T, K), np.float32)
+    for t in range(c.T):
+        js = ent[off[t]:off[t + 1]]
+        slot[t, :len(js)] = js
+        w[t, :len(js)] = c.weights.ravel()[js]
+    ref = brute.combine_f64(y.reshape(c.E * c.C, 16), slot, w)
+    assert np.array_equal(out, ref)
+    # token subset form returns the same rows
+    sub = np.array([3, 0, 29, 3], np.int32)
+    assert np.array_equal(oracle.ec_combine(y, c.weights, c.token_indices, c.T, tokens=sub), out[sub])
