@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE token dispatch/combine hot path on one MI355X.
+
+One step = ep_get_dispatch_layout + ep_dispatch (bf16, expert-contiguous
+receive buffer) + ep_combine (routing weights, identity experts: y = the
+receive buffer) on the prefill-shaped workload T=4096, H=7168, E=256, top-8
+with Zipf-skewed routing.  Inputs are seeded synthetic tensors, resident in
+HBM before the timed region.  W untimed warm-up steps, then exactly K timed
+steps between two device synchronisations; rank 0 prints one JSON line.
+
+Also reported: per-operation times (HIP events on the stream the kernels run
+on), the roofline of the dominant kernel (algorithmic bytes per launch over
+its average duration, against 8 TB/s), HBM traffic from the committed
+rocprofv3 counter summary when it was taken on the current kernel source,
+and the CPU oracle timed on the host on a bounded sample of the same
+workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine tokens/s & achieved HBM GB/s, T=4096 H=7168 E=256 top-8"
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_T4096_H7168_E256_K8.json")
+
+
+def kernel_source_hash():
+    d = os.path.join(ROOT, "combine_get_dispatch_04_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def traffic_entry(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when that summary was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("src_sha256") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(c, budget_s):
+    """The oracle as it stands (single thread) on full passes of the same
+    workload until `budget_s` seconds have elapsed."""
+    import oracle
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        L = oracle.layout(c.topk_idx, c.E)
+        slot, _, _ = oracle.slots(c.topk_idx, c.E, False, c.T * c.K)
+        y = oracle.dispatch_bf16(c.x, slot, int(L["offsets"][-1]))
+        oracle.combine(y, slot, c.topk_weights)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": reps * c.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full pass(es) of the same workload (layout, slots, bf16 dispatch, "
+                      f"weighted combine; {c.T} tokens each), {el:.1f} s on one host thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="write this many MiB of scratch before each step (cold caches)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the multi-GPU "
+              "exchange is not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import combine_get_dispatch_04_amd._native as N
+    from combine_get_dispatch_04_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = W.prefill()
+    T, H, E, K = c.T, c.H, c.E, c.K
+    x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    idx = torch.from_numpy(c.topk_idx).to(dev)
+    w = torch.from_numpy(c.topk_weights).to(dev)
+    rows = T * K
+    N_valid = int((c.topk_idx >= 0).sum())
+    ws_bytes = N.ep_workspace_bytes(T, K, E, 1)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    tpr = torch.empty(1, dtype=torch.int32, device=dev)
+    itr = torch.empty((T, 1), dtype=torch.uint8, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    recv = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+    src = torch.empty(rows, dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    flush = torch.empty(a.flush_mib << 20, dtype=torch.uint8, device=dev) if a.flush_mib else None
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    P = lambda t: t.data_ptr()
+
+    def layout():
+        N.ep_get_dispatch_layout(P(idx), T, K, E, 1, P(counts), P(offsets), P(tpr), P(itr),
+                                 P(ninv), P(ws), ws_bytes, sp)
+
+    def dispatch():
+        N.ep_dispatch(P(x), T, H, P(idx), K, E, P(offsets), N.EP_LAYOUT_CONTIGUOUS, rows,
+                      N.EP_QUANT_BF16, P(recv), None, P(slot), P(src), P(nd), P(ws), ws_bytes, sp)
+
+    def combine():
+        N.ep_combine(P(recv), rows, H, P(slot), P(w), T, K, P(out), sp)
+
+    for _ in range(a.warmup):
+        layout(); dispatch(); combine()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    t_steps = []
+    torch.cuda.synchronize()
+    if flush is None:
+        t0 = time.perf_counter()
+        for i in range(a.steps):
+            e = ev[i]
+            e[0].record(stream); layout()
+            e[1].record(stream); dispatch()
+            e[2].record(stream); combine()
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    else:
+        for i in range(a.steps):
+            flush.fill_(i & 0xFF)
+            e = ev[i]
+            e[0].record(stream); layout()
+            e[1].record(stream); dispatch()
+            e[2].record(stream); combine()
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        wall_ms = None
+    lay_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    dis_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    com_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    ms_per_step = wall_ms if wall_ms is not None else float(step_ms.mean())
+
+    # algorithmic bytes (each x row read once, each received row written once
+    # and read once, each output row written once, plus index metadata)
+    row = H * 2
+    meta = 5 * T * K * 4
+    alg_total = T * row + N_valid * row + N_valid * row + T * row + meta
+    alg_dispatch = T * row + N_valid * row + 2 * T * K * 4
+    alg_combine = N_valid * row + T * row + 2 * T * K * 4
+    d_us, c_us = dis_ms.mean() * 1e3, com_ms.mean() * 1e3
+    if d_us >= c_us:
+        dom, dom_us, dom_bytes = "dispatch_kernel", d_us, alg_dispatch
+    else:
+        dom, dom_us, dom_bytes = "combine_kernel", c_us, alg_combine
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    traffic = traffic_entry(dom)
+
+    torch.cuda.synchronize()
+    res = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": c.name, "T": T, "H": H, "E": E, "top_k": K,
+                   "routing": "top-8 of N(0,1) logits + 2*log Zipf(1.2) expert bias",
+                   "recv_layout": "contiguous", "quant": "bf16", "combine": "weighted",
+                   "valid_slots": N_valid, "cold_flush_mib": a.flush_mib},
+        "achieved_GBps": alg_total / (ms_per_step * 1e-3) / 1e9,
+        "frac_of_peak_hbm": alg_total / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "algorithmic_bytes_per_step": alg_total,
+        "per_op_us": {"layout": float(lay_ms.mean() * 1e3), "dispatch": float(d_us),
+                      "combine": float(c_us), "step_events": float(step_ms.mean() * 1e3),
+                      "step_p10": float(np.percentile(step_ms, 10) * 1e3),
+                      "step_p90": float(np.percentile(step_ms, 90) * 1e3)},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "avg_launch_us": float(dom_us)},
+    }
+    if a.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(c, a.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

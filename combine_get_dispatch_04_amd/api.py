@@ -1,0 +1,192 @@
+"""Torch-tensor front end over the libep C ABI.
+
+Mirrors the Buffer methods of the "DeepEP-Ascend" README ("API Overview":
+get_dispatch_layout, dispatch, combine, low_latency_dispatch /
+low_latency_combine) and the expert-centric calls asked for in "[Feature
+Request] Support Expert-Choice Routing via Native Expert-Centric API"
+(Solution 1: dispatch_expert_choice with token_indices [E, C] and weights).
+
+torch only allocates device memory and supplies the current stream; every
+step runs in the HIP kernels of libep.so.  Errors from the library raise
+EpError (a ValueError).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _native as N
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class Layout:
+    """Result of get_dispatch_layout.  The workspace carries per-chunk tables
+    to the dispatch that follows and must not be reused before it."""
+    num_tokens_per_rank: torch.Tensor          # [R] int32
+    num_tokens_per_rdma_rank: None             # needs a node topology: not produced
+    num_tokens_per_expert: torch.Tensor        # [E] int32 (count form)
+    is_token_in_rank: torch.Tensor             # [T, R] uint8
+    offsets: torch.Tensor                      # [E+1] int32 (prefix-sum form)
+    num_invalid: torch.Tensor                  # [1] int32
+    topk_idx: torch.Tensor
+    num_experts: int
+    num_ranks: int
+    workspace: torch.Tensor
+
+
+@dataclass
+class Handle:
+    """What combine needs from dispatch: the receive row of every (t, k)."""
+    slot: torch.Tensor                         # [T, K] int32, -1 = not received
+    recv_src: torch.Tensor                     # [rows] int32, source token of each written row
+    num_dropped: torch.Tensor                  # [1] int32
+    rows: int
+    recv_layout: str
+    cap: Optional[int]
+
+
+@dataclass
+class ExpertChoiceHandle:
+    tok_off: torch.Tensor                      # [T+1] int32
+    tok_ent: torch.Tensor                      # [E*C] int32
+    weights: torch.Tensor                      # [E, C] float32
+    num_invalid: torch.Tensor                  # [1] int32
+    num_tokens: int
+
+
+def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int = 1) -> Layout:
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    T, K = topk_idx.shape
+    E, R = int(num_experts), int(num_ranks)
+    dev = topk_idx.device
+    ws_bytes = N.ep_workspace_bytes(T, K, E, R)
+    if ws_bytes == 0:
+        raise N.EpError("ep_workspace_bytes", N.EP_ERR_INVALID_ARG)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    tpr = torch.empty(R, dtype=torch.int32, device=dev)
+    itr = torch.empty((T, R), dtype=torch.uint8, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    N.ep_get_dispatch_layout(_ptr(topk_idx), T, K, E, R, _ptr(counts), _ptr(offsets), _ptr(tpr),
+                             _ptr(itr), _ptr(ninv), _ptr(ws), ws_bytes, _stream())
+    return Layout(tpr, None, counts, itr, offsets, ninv, topk_idx, E, R, ws)
+
+
+def dispatch(x: torch.Tensor, layout: Layout, *, quant: str = "bf16",
+             recv_layout: str = "contiguous", cap: Optional[int] = None,
+             max_rows: Optional[int] = None):
+    """-> (recv_x, recv_scales or None, Handle).
+
+    recv_layout "contiguous": expert blocks back to back, `max_rows` rows
+    (default T*K, always enough).  "padded": [E, cap] rows, the low-latency
+    form.  quant "bf16" or "fp8_e4m3_g128" (e4m3 codes + fp32 scale per 128
+    channels)."""
+    _need(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    idx = layout.topk_idx
+    if idx.shape[0] != T:
+        raise ValueError("x and topk_idx disagree on the number of tokens")
+    K, E = idx.shape[1], layout.num_experts
+    if quant == "bf16":
+        q, rdt = N.EP_QUANT_BF16, torch.bfloat16
+    elif quant == "fp8_e4m3_g128":
+        q, rdt = N.EP_QUANT_FP8_E4M3_G128, torch.float8_e4m3fn
+    else:
+        raise ValueError(f"unknown quant mode {quant!r}")
+    if recv_layout == "contiguous":
+        lay, arg = N.EP_LAYOUT_CONTIGUOUS, (T * K if max_rows is None else int(max_rows))
+        rows = arg
+    elif recv_layout == "padded":
+        if cap is None:
+            raise ValueError("padded layout needs cap")
+        lay, arg = N.EP_LAYOUT_PADDED, int(cap)
+        rows = E * arg
+    else:
+        raise ValueError(f"unknown receive layout {recv_layout!r}")
+    dev = x.device
+    recv = torch.empty((rows, H), dtype=rdt, device=dev)
+    scales = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if q else None
+    slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+    src = torch.empty(rows, dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    N.ep_dispatch(_ptr(x), T, H, _ptr(idx), K, E, _ptr(layout.offsets), lay, arg, q, _ptr(recv),
+                  _ptr(scales), _ptr(slot), _ptr(src), _ptr(nd), _ptr(layout.workspace),
+                  layout.workspace.numel(), _stream())
+    return recv, scales, Handle(slot, src, nd, rows, recv_layout, cap if lay else None)
+
+
+def combine(y: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[t] = bf16(sum_k w[t,k] * y[slot[t,k]]), fp32 sums; w = 1 if None."""
+    _need(y, "y", torch.bfloat16, 2)
+    T, K = handle.slot.shape
+    H = y.shape[1]
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, 2)
+        if tuple(topk_weights.shape) != (T, K):
+            raise ValueError("topk_weights must be [T, K]")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    N.ep_combine(_ptr(y), y.shape[0], H, _ptr(handle.slot), _ptr(topk_weights), T, K, _ptr(out),
+                 _stream())
+    return out
+
+
+def dispatch_expert_choice(x: torch.Tensor, token_indices: torch.Tensor, weights: torch.Tensor):
+    """-> (recv_x [E, C, H], ExpertChoiceHandle).  The weights are kept in the
+    handle and applied by combine_expert_choice."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(token_indices, "token_indices", torch.int32, 2)
+    _need(weights, "weights", torch.float32, 2)
+    T, H = x.shape
+    E, C = token_indices.shape
+    if tuple(weights.shape) != (E, C):
+        raise ValueError("weights must be [E, C] like token_indices")
+    dev = x.device
+    ws_bytes = N.ep_ec_workspace_bytes(T, E, C)
+    if ws_bytes == 0:
+        raise N.EpError("ep_ec_workspace_bytes", N.EP_ERR_INVALID_ARG)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    recv = torch.empty((E, C, H), dtype=torch.bfloat16, device=dev)
+    off = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    ent = torch.empty(E * C, dtype=torch.int32, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    N.ep_dispatch_expert_choice(_ptr(x), T, H, _ptr(token_indices), E, C, _ptr(recv), _ptr(off),
+                                _ptr(ent), _ptr(ninv), _ptr(ws), ws_bytes, _stream())
+    return recv, ExpertChoiceHandle(off, ent, weights, ninv, T)
+
+
+def combine_expert_choice(y: torch.Tensor, handle: ExpertChoiceHandle,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(y, "y", torch.bfloat16, 3)
+    E, C, H = y.shape
+    T = handle.num_tokens
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    N.ep_combine_expert_choice(_ptr(y), _ptr(handle.weights), E, C, H, _ptr(handle.tok_off),
+                               _ptr(handle.tok_ent), T, _ptr(out), _stream())
+    return out

@@ -1,0 +1,201 @@
+// ep_combine.hip -- weighted gather-reduce back to token order.
+//   Token choice ("DeepEP-Ascend" README, API Overview: combine through the
+//   dispatch handle; low_latency_combine also takes topk_weights):
+//     out[t] = bf16( sum_k w[t,k] * y[slot[t,k]] )
+//   Expert choice ("[Feature Request] Support Expert-Choice Routing via
+//   Native Expert-Centric API", Solution 1: weights with the expert-centric
+//   indices):
+//     out[t] = bf16( sum over token t's entries j of w[j] * y[j] )
+//
+// One block per (token, row segment); each thread owns PPT 16-byte pieces
+// (8 channels each) and keeps 8*PPT fp32 accumulators.  For every source row
+// (block-uniform, so the row index and the weight are scalar loads) it loads
+// its pieces with non-temporal loads (each y row is read once) and
+// accumulates with fp32 FMAs in ascending k / entry order, then rounds once
+// to bf16 (nearest even).  A token with no source row writes +0.
+#include "ep_common.h"
+#include "ep_internal.h"
+
+namespace ep {
+
+namespace {
+
+template <int PPT>
+__device__ __forceinline__ void acc_row(float (&acc)[PPT][8], const char *src, float wk, int seg0,
+                                        int pieces)
+{
+    u32x4 v[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        int i = seg0 + threadIdx.x + j * blockDim.x;
+        v[j] = i < pieces ? ld16_nt(src + (size_t)i * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        acc[j][0] = fmaf(wk, bf16_lo(v[j].x), acc[j][0]);
+        acc[j][1] = fmaf(wk, bf16_hi(v[j].x), acc[j][1]);
+        acc[j][2] = fmaf(wk, bf16_lo(v[j].y), acc[j][2]);
+        acc[j][3] = fmaf(wk, bf16_hi(v[j].y), acc[j][3]);
+        acc[j][4] = fmaf(wk, bf16_lo(v[j].z), acc[j][4]);
+        acc[j][5] = fmaf(wk, bf16_hi(v[j].z), acc[j][5]);
+        acc[j][6] = fmaf(wk, bf16_lo(v[j].w), acc[j][6]);
+        acc[j][7] = fmaf(wk, bf16_hi(v[j].w), acc[j][7]);
+    }
+}
+
+template <int PPT>
+__device__ __forceinline__ void store_row(const float (&acc)[PPT][8], uint16_t *out, int H, int t,
+                                          int seg0, int pieces)
+{
+    char *dst = reinterpret_cast<char *>(out) + (size_t)t * H * 2;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        int i = seg0 + threadIdx.x + j * blockDim.x;
+        if (i < pieces) {
+            u32x4 o;
+            o.x = pack_bf16x2(acc[j][0], acc[j][1]);
+            o.y = pack_bf16x2(acc[j][2], acc[j][3]);
+            o.z = pack_bf16x2(acc[j][4], acc[j][5]);
+            o.w = pack_bf16x2(acc[j][6], acc[j][7]);
+            st16(dst + (size_t)i * 16, o);
+        }
+    }
+}
+
+template <int PPT>
+__global__ void __launch_bounds__(256)
+combine_kernel(const uint16_t *__restrict__ y, int y_rows, int H,
+               const int32_t *__restrict__ slot, const float *__restrict__ w, int K,
+               uint16_t *__restrict__ out)
+{
+    const int t = blockIdx.x;
+    const int pieces = H >> 3;
+    const int seg0 = blockIdx.y * PPT * blockDim.x;
+    float acc[PPT][8];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            acc[j][u] = 0.0f;
+    const int32_t *srow = slot + (int64_t)t * K;
+    const float *wrow = w ? w + (int64_t)t * K : nullptr;
+    for (int k = 0; k < K; ++k) {
+        const int s = srow[k];
+        if ((unsigned)s >= (unsigned)y_rows)
+            continue;
+        const float wk = wrow ? wrow[k] : 1.0f;
+        acc_row<PPT>(acc, reinterpret_cast<const char *>(y) + (size_t)s * H * 2, wk, seg0, pieces);
+    }
+    store_row<PPT>(acc, out, H, t, seg0, pieces);
+}
+
+template <int PPT>
+__global__ void __launch_bounds__(256)
+ec_combine_kernel(const uint16_t *__restrict__ y, const float *__restrict__ w, int n_ent, int H,
+                  const int32_t *__restrict__ tok_off, const int32_t *__restrict__ tok_ent,
+                  uint16_t *__restrict__ out)
+{
+    const int t = blockIdx.x;
+    const int pieces = H >> 3;
+    const int seg0 = blockIdx.y * PPT * blockDim.x;
+    float acc[PPT][8];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            acc[j][u] = 0.0f;
+    const int b = tok_off[t], e = tok_off[t + 1];
+    const int n = (b >= 0 && e >= b && e <= n_ent) ? e - b : 0;
+    for (int a = 0; a < n; ++a) {
+        const int j = tok_ent[b + a];
+        if ((unsigned)j >= (unsigned)n_ent)
+            continue;
+        acc_row<PPT>(acc, reinterpret_cast<const char *>(y) + (size_t)j * H * 2, w[j], seg0,
+                     pieces);
+    }
+    store_row<PPT>(acc, out, H, t, seg0, pieces);
+}
+
+struct RowShape {
+    int bd, ppt, nseg;
+};
+
+// Fewest idle lanes over block sizes 256/128/64 with at most `maxppt`
+// pieces per thread; more row segments (grid.y) when a row is longer.
+RowShape row_shape(int pieces, int maxppt)
+{
+    RowShape best{64, 1, 1};
+    long long best_waste = -1;
+    for (int bd : {256, 128, 64}) {
+        int ppt = (pieces + bd - 1) / bd;
+        if (ppt < 1)
+            ppt = 1;
+        if (ppt > maxppt)
+            ppt = maxppt;
+        int nseg = (pieces + ppt * bd - 1) / (ppt * bd);
+        if (nseg < 1)
+            nseg = 1;
+        long long waste = (long long)nseg * ppt * bd - pieces;
+        if (best_waste < 0 || waste < best_waste) {
+            best = {bd, ppt, nseg};
+            best_waste = waste;
+        }
+    }
+    return best;
+}
+
+}  // namespace
+
+#define EP_PPT_SWITCH(PPT_VAR, CASE) \
+    switch (PPT_VAR) {               \
+        CASE(1)                      \
+        CASE(2)                      \
+        CASE(3)                      \
+        CASE(4)                      \
+        CASE(5)                      \
+        CASE(6)                      \
+        CASE(7)                      \
+        CASE(8)                      \
+    default:                         \
+        return hipErrorInvalidValue; \
+    }
+
+hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot,
+                          const float *w, int T, int K, uint16_t *out, hipStream_t s)
+{
+    if (T == 0)
+        return hipSuccess;
+    RowShape rs = row_shape(H / 8, 8);
+    dim3 grid(T, rs.nseg), block(rs.bd);
+#define EP_COMBINE_CASE(N)                                                                       \
+    case N:                                                                                      \
+        hipLaunchKernelGGL((combine_kernel<N>), grid, block, 0, s, y, y_rows, H, slot, w, K,  \
+                           out);                                                         \
+        break;
+    EP_PPT_SWITCH(rs.ppt, EP_COMBINE_CASE)
+#undef EP_COMBINE_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_ec_combine(const uint16_t *y, const float *w, int E, int C, int H,
+                             const int32_t *tok_off, const int32_t *tok_ent, int T,
+                             uint16_t *out, hipStream_t s)
+{
+    if (T == 0)
+        return hipSuccess;
+    // Tokens picked by many experts read many rows: spread each row over
+    // more blocks (fewer pieces per thread) so a popular token's work is
+    // shared by several CUs.
+    RowShape rs = row_shape(H / 8, 2);
+    dim3 grid(T, rs.nseg), block(rs.bd);
+#define EP_EC_COMBINE_CASE(N)                                                                    \
+    case N:                                                                                      \
+        hipLaunchKernelGGL((ec_combine_kernel<N>), grid, block, 0, s, y, w, E * C, H, tok_off,    \
+                           tok_ent, out);                                                        \
+        break;
+    EP_PPT_SWITCH(rs.ppt, EP_EC_COMBINE_CASE)
+#undef EP_EC_COMBINE_CASE
+    return hipGetLastError();
+}
+
+}  // namespace ep

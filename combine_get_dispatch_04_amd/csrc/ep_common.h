@@ -1,0 +1,139 @@
+// ep_common.h -- device helpers shared by the libep kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+constexpr int kWave = 64;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- memory
+// 16-byte row pieces.  Streams that are written once and not read again by
+// the same kernel use non-temporal stores so they do not displace inputs
+// that are still being read from the caches.
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ u32x4 ld16_nt(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+__device__ __forceinline__ void st16_nt(void *p, u32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+__device__ __forceinline__ void st8_nt(void *p, u32x2 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
+}
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs): add half an ulp
+// of the kept part minus one, plus the kept part's lowest bit, then truncate.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ---------------------------------------------------------------- e4m3
+// fp32 -> OCP E4M3 code (bias 7, 3 mantissa bits, max finite 448, no inf),
+// round to nearest even.  Below 2^-6 the code is the subnormal count
+// m = round(|v| * 2^9) (exact scaling, hardware round-to-nearest-even; m = 8
+// is the code of 2^-6, so the ranges join).  From 2^-6 up, the fp32 pattern
+// is rounded to 3 mantissa bits in place (a carry moves into the exponent)
+// and the exponent is rebiased from 127 to 7.  |v| >= 464 saturates to 448.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x43E80000u) {                 // 464.0
+        code = 0x7Eu;
+    } else if (a < 0x3C800000u) {           // 2^-6
+        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    } else {
+        uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+        code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);   // exponent - 127 + 7
+    }
+    return sign | code;
+}
+
+// ---------------------------------------------------------------- waves
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ uint64_t lanemask_lt(int lane)
+{
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Lanes of this wave whose `key` equals mine, among lanes where `active`
+// holds.  gfx950 has no match instruction: one ballot per key bit narrows
+// the set.  Must be called by all lanes of the wave (converged).
+__device__ __forceinline__ uint64_t match_key(int key, bool active, int nbits)
+{
+    uint64_t m = ballot(active);
+    for (int b = 0; b < nbits; ++b) {
+        bool bit = (key >> b) & 1;
+        uint64_t bb = ballot(active && bit);
+        m &= bit ? bb : ~bb;
+    }
+    return active ? m : 0ull;
+}
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
+{
+    for (int o = 1; o < kWave; o <<= 1) {
+        int n = __shfl_up(v, o, kWave);
+        if (lane >= o)
+            v += n;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over a block's threads (blockDim.x <= 1024, multiple
+// of 64).  `tmp` holds >= 17 ints of shared memory.  Returns my exclusive
+// prefix; *total receives the block sum.  All threads must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *tmp, int *total)
+{
+    int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    int nw = blockDim.x / kWave;
+    int inc = wave_inclusive_scan(v, lane);
+    if (lane == kWave - 1)
+        tmp[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        int s = lane < nw ? tmp[lane] : 0;
+        int si = wave_inclusive_scan(s, lane);
+        if (lane < nw)
+            tmp[lane] = si - s;
+        if (lane == kWave - 1)
+            tmp[16] = si;
+    }
+    __syncthreads();
+    int ex = tmp[wave] + inc - v;
+    *total = tmp[16];
+    __syncthreads();
+    return ex;
+}
+
+}  // namespace ep

@@ -1,0 +1,53 @@
+// ep_internal.h -- host-side plans and launchers shared by the libep sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+// How the layout splits topk_idx: blocks ("chunks") of CT whole tokens.
+// Inside a chunk, `waves` waves each take a contiguous run of entries.
+struct LayoutPlan {
+    int T, K, E, R;
+    int CT;        // tokens per chunk
+    int nchunk;    // ceil(T / CT)
+    int waves;     // waves per chunk block
+    int nbits;     // bits needed for an expert id in [0, E)
+    size_t lds;    // dynamic shared memory of the chunk kernel
+    // workspace carve-up (byte offsets, 256-aligned)
+    size_t off_hist, off_rank, off_rpart, off_ipart, bytes;
+};
+
+LayoutPlan make_layout_plan(int T, int K, int E, int R);
+
+struct EcPlan {
+    int T, E, C;
+    size_t off_cnt, off_cursor, off_tmp, off_misc, bytes;
+};
+EcPlan make_ec_plan(int T, int E, int C);
+
+hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *counts,
+                         int32_t *offsets, int32_t *tokens_per_rank, uint8_t *is_token_in_rank,
+                         int32_t *num_invalid, char *ws, hipStream_t s);
+
+hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const int32_t *topk_idx,
+                           const int32_t *offsets, bool padded, int cap_or_rows, bool fp8,
+                           void *recv_x, float *recv_scales, int32_t *slot, int32_t *recv_src,
+                           int32_t *num_dropped, char *ws, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot,
+                          const float *w, int T, int K, uint16_t *out, hipStream_t s);
+
+hipError_t launch_ec_dispatch(const EcPlan &p, const uint16_t *x, int H,
+                              const int32_t *token_indices, uint16_t *recv_x, int32_t *tok_off,
+                              int32_t *tok_ent, int32_t *num_invalid, char *ws, hipStream_t s);
+
+hipError_t launch_ec_combine(const uint16_t *y, const float *w, int E, int C, int H,
+                             const int32_t *tok_off, const int32_t *tok_ent, int T,
+                             uint16_t *out, hipStream_t s);
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+}  // namespace ep

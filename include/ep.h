@@ -1,0 +1,197 @@
+/*
+ * ep.h -- C ABI of libep: MoE token dispatch/combine on one MI355X (gfx950).
+ *
+ * The operations follow two pages:
+ *   [EPA] "DeepEP-Ascend" README: the "API Overview" table
+ *         (get_dispatch_layout, dispatch, combine, low_latency_dispatch,
+ *         low_latency_combine), the "Environment Variables" table
+ *         (MOE_EXPERT_TOKEN_NUMS_TYPE: per-expert count or prefix sum;
+ *         MOE_ENABLE_TOPK_NEG_ONE: a -1 in topk_idx means "not dispatched")
+ *         and the "Quantization Modes in Normal Dispatch" table
+ *         (float8_e4m3fn payload with float32 scales).
+ *   [ECR] "[Feature Request] Support Expert-Choice Routing via Native
+ *         Expert-Centric API ([num_experts, capacity])", "Proposed
+ *         Solutions", Solution 1: token_indices [num_experts, capacity]
+ *         int32 picked by each expert, plus per-entry expert weights.
+ *
+ * Conventions for every entry point
+ *   - Notation: T tokens, H hidden channels, E experts, K = num_topk,
+ *     R ranks (experts split into R equal contiguous blocks), C capacity,
+ *     N = number of valid (t,k) slots.
+ *   - bf16 values travel as uint16_t bit patterns, fp8 e4m3 as uint8_t codes.
+ *   - Every array pointer is DEVICE memory, row-major, owned by the caller;
+ *     libep allocates nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously.  Outputs are valid once the stream reaches
+ *     the end of the call's work.
+ *   - Argument errors are found on the host before anything is enqueued and
+ *     returned synchronously (EP_ERR_INVALID_ARG / EP_ERR_UNSUPPORTED /
+ *     EP_ERR_WORKSPACE).  A failed launch returns EP_ERR_HIP.  Bad DATA
+ *     (an index out of range, a capacity overflow) never fails a call: it
+ *     is counted in num_invalid / num_dropped and skipped, so every output
+ *     stays defined.
+ *   - Array base pointers must be 16-byte aligned; `ws` 256-byte aligned.
+ *   - H % 8 == 0 (rows move in 16-byte pieces); T*K, E*C, rows*H < 2^31.
+ *   - Results are deterministic: the same inputs give the same bytes.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARG = 1,   /* a size, pointer or alignment is wrong */
+    EP_ERR_UNSUPPORTED = 2,   /* a valid request outside what is built (e.g. E > 4096) */
+    EP_ERR_WORKSPACE = 3,     /* ws is NULL, misaligned or smaller than required */
+    EP_ERR_HIP = 4            /* the HIP runtime reported a launch error */
+} ep_status_t;
+
+typedef enum {
+    EP_LAYOUT_CONTIGUOUS = 0, /* expert blocks back to back: expert e's rows start at offsets[e] */
+    EP_LAYOUT_PADDED = 1      /* [E, cap] rows: expert e's rows start at e*cap (low-latency form) */
+} ep_recv_layout_t;
+
+typedef enum {
+    EP_QUANT_BF16 = 0,          /* rows copied as bf16 */
+    EP_QUANT_FP8_E4M3_G128 = 1  /* e4m3 codes + one fp32 scale per 128 channels */
+} ep_quant_t;
+
+/* Human-readable name of a status code (static string). */
+const char *ep_status_string(ep_status_t status);
+
+/* Bytes of device workspace that ep_get_dispatch_layout + ep_dispatch need
+ * for these sizes (0 is never returned for valid sizes). */
+size_t ep_workspace_bytes(int T, int K, int E, int R);
+
+/* Bytes of device workspace that ep_dispatch_expert_choice needs. */
+size_t ep_ec_workspace_bytes(int T, int E, int C);
+
+/*
+ * ep_get_dispatch_layout -- [EPA] API Overview, get_dispatch_layout; the
+ * count and prefix-sum forms of [EPA] Environment Variables.
+ *
+ *   topk_idx          [T, K] int32 in.  -1 = not dispatched; any other value
+ *                     outside [0, E) is invalid (counted, then ignored).
+ *   counts            [E] int32 out: valid (t,k) per expert.
+ *   offsets           [E+1] int32 out: exclusive prefix sum, offsets[E] = N.
+ *   tokens_per_rank   [R] int32 out or NULL: tokens with >= 1 valid slot on
+ *                     rank r (rank r owns experts [r*E/R, (r+1)*E/R)).
+ *   is_token_in_rank  [T, R] uint8 out or NULL: 1 if token t has >= 1 valid
+ *                     slot on rank r, else 0.
+ *   num_invalid       [1] int32 out: entries that are neither -1 nor in [0,E).
+ *   ws, ws_bytes      workspace of >= ep_workspace_bytes(T, K, E, R) bytes.
+ *                     It carries per-chunk tables to the following
+ *                     ep_dispatch, which must get the same ws, topk_idx, T,
+ *                     K and E on the same stream with no other use of ws in
+ *                     between.
+ * Constraints: T >= 0, K >= 1, 1 <= E <= 4096, 1 <= R <= 1024, E % R == 0.
+ */
+ep_status_t ep_get_dispatch_layout(const int32_t *topk_idx, int T, int K, int E, int R,
+                                   int32_t *counts, int32_t *offsets,
+                                   int32_t *tokens_per_rank, uint8_t *is_token_in_rank,
+                                   int32_t *num_invalid, void *ws, size_t ws_bytes,
+                                   void *stream);
+
+/*
+ * ep_dispatch -- [EPA] API Overview, dispatch (contiguous receive buffer)
+ * and low_latency_dispatch (per-expert capacity); [EPA] Quantization Modes
+ * (bf16, or float8_e4m3fn with float32 scales).
+ *
+ * The receive row ("slot") of a valid (t,k) with expert e is found by a
+ * stable counting sort: r = number of valid (t',k') before (t,k) in
+ * row-major order with the same expert.
+ *   EP_LAYOUT_CONTIGUOUS: slot = offsets[e] + r, kept if slot < rows
+ *                         (rows = cap_or_max_rows; T*K always suffices).
+ *   EP_LAYOUT_PADDED:     slot = e*cap + r, kept if r < cap
+ *                         (cap = cap_or_max_rows; rows = E*cap).
+ * Slots that are not kept are -1 and counted in num_dropped; padding and
+ * invalid entries are -1 and not counted.  For each kept slot:
+ *   EP_QUANT_BF16:          recv_x[slot, :] = x[t, :]  (bf16 bits, [rows, H])
+ *   EP_QUANT_FP8_E4M3_G128: per token and 128-channel group g, with
+ *                           a = max|x| over the group: s = a / 448 in fp32
+ *                           (0 when a == 0), q = e4m3(x / s) rounded to
+ *                           nearest even with fp32 division (all zero when
+ *                           a == 0); recv_x[slot, :] = q (uint8 [rows, H]),
+ *                           recv_scales[slot, g] = s (fp32 [rows, H/128]).
+ *                           Needs H % 128 == 0.
+ *   x            [T, H] bf16 in.
+ *   topk_idx     [T, K] int32 in (the array given to ep_get_dispatch_layout).
+ *   offsets      [E+1] int32 in, from ep_get_dispatch_layout.
+ *   recv_x       [rows, H] out; rows that receive no token are not written.
+ *   recv_scales  [rows, H/128] fp32 out (fp8 only; NULL for bf16).
+ *   slot         [T, K] int32 out: the handle for ep_combine.
+ *   recv_src     [rows] int32 out or NULL: recv_src[slot] = t for kept slots;
+ *                other entries are not written.
+ *   num_dropped  [1] int32 out.
+ *   ws, ws_bytes the workspace just used by ep_get_dispatch_layout.
+ */
+ep_status_t ep_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx, int K, int E,
+                        const int32_t *offsets, ep_recv_layout_t layout, int cap_or_max_rows,
+                        ep_quant_t quant, void *recv_x, float *recv_scales,
+                        int32_t *slot, int32_t *recv_src, int32_t *num_dropped,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * ep_combine -- [EPA] API Overview, combine (reduce through the dispatch
+ * handle) and low_latency_combine (also takes topk_weights).
+ *   out[t, :] = bf16( sum over k with slot[t,k] >= 0 of w[t,k] * y[slot[t,k], :] )
+ * summed in fp32, rounded to nearest even; a token with no kept slot gives +0.
+ *   y             [y_rows, H] bf16 in, rows indexed like recv_x.
+ *   slot          [T, K] int32 in, from ep_dispatch; entries outside
+ *                 [0, y_rows) are skipped like -1 (a malformed handle cannot
+ *                 make the kernel read outside y).
+ *   topk_weights  [T, K] fp32 in, or NULL for unit weights (a plain sum).
+ *   out           [T, H] bf16 out; must not overlap y.
+ */
+ep_status_t ep_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot,
+                       const float *topk_weights, int T, int K, uint16_t *out, void *stream);
+
+/*
+ * ep_dispatch_expert_choice -- [ECR] Solution 1.
+ *   recv_x[e, c, :] = x[token_indices[e, c], :] for entries in [0, T);
+ *   -1 entries are empty and leave their row unwritten; other values are
+ *   invalid (counted in num_invalid, row unwritten).  Duplicates are allowed.
+ * It also builds the inverse map kept as the handle for combine:
+ *   tok_off [T+1] int32 out, tok_ent [E*C] int32 out: token t's flat entries
+ *   j = e*C + c, ascending, are tok_ent[tok_off[t] .. tok_off[t+1]);
+ *   tok_off[T] = number of valid entries; tok_ent beyond it is not written.
+ *   x             [T, H] bf16 in.
+ *   token_indices [E, C] int32 in.
+ *   recv_x        [E, C, H] bf16 out.
+ *   num_invalid   [1] int32 out.
+ *   ws, ws_bytes  workspace of >= ep_ec_workspace_bytes(T, E, C) bytes.
+ * No limit on how many experts pick one token.
+ */
+ep_status_t ep_dispatch_expert_choice(const uint16_t *x, int T, int H,
+                                      const int32_t *token_indices, int E, int C,
+                                      uint16_t *recv_x, int32_t *tok_off, int32_t *tok_ent,
+                                      int32_t *num_invalid, void *ws, size_t ws_bytes,
+                                      void *stream);
+
+/*
+ * ep_combine_expert_choice -- [ECR] Solution 1 (the weights passed with the
+ * expert-centric indices).
+ *   out[t, :] = bf16( sum over j in tok_ent[tok_off[t] .. tok_off[t+1]) of
+ *                     weights[j] * y[j, :] ), fp32 sums, nearest-even rounding;
+ *   tokens that no expert picked give +0.
+ *   y        [E, C, H] bf16 in.     weights [E, C] fp32 in.
+ *   tok_off, tok_ent                from ep_dispatch_expert_choice; a token
+ *            whose range is not inside [0, E*C], and entries outside
+ *            [0, E*C), contribute nothing.
+ *   out      [T, H] bf16 out; must not overlap y.
+ */
+ep_status_t ep_combine_expert_choice(const uint16_t *y, const float *weights, int E, int C, int H,
+                                     const int32_t *tok_off, const int32_t *tok_ent, int T,
+                                     uint16_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

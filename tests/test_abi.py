@@ -1,0 +1,190 @@
+"""C-ABI checks that need no GPU: every symbol declared in include/ep.h is
+exported by libep.so with the binding's arity; workspace sizing; and every
+argument error is returned synchronously, before any launch.
+
+Pointers below are fake, aligned addresses: every call here is rejected by
+the host-side checks, so nothing is dereferenced or launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import combine_get_dispatch_04_amd._native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(ep_\w+)\s*\(([^;{]*?)\)\s*;", src):
+        args = [a for a in m.group(2).split(",") if a.strip() and a.strip() != "void"]
+        out[m.group(1)] = len(args)
+    return out
+
+
+def test_header_declares_the_five_operations():
+    d = _declared()
+    for name in ("ep_get_dispatch_layout", "ep_dispatch", "ep_combine",
+                 "ep_dispatch_expert_choice", "ep_combine_expert_choice"):
+        assert name in d
+
+
+def test_every_declared_symbol_is_exported_with_binding_arity():
+    L = N.lib()
+    d = _declared()
+    assert set(d) == set(N.SIGNATURES)
+    for name, nargs in d.items():
+        assert hasattr(L, name), name
+        assert len(N.SIGNATURES[name][1]) == nargs, name
+    syms = subprocess.run(["nm", "-D", "--defined-only", N.LIB_PATH], capture_output=True,
+                          text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in syms.splitlines() if " T " in ln}
+    assert set(d) <= exported
+
+
+def test_status_strings():
+    for s in range(5):
+        assert N.status_string(s)
+    assert N.status_string(0) == "ok"
+
+
+def test_workspace_sizes():
+    a = N.ep_workspace_bytes(4096, 8, 256, 1)
+    assert a > 4096 * 8 * 4 and a % 256 == 0
+    assert N.ep_workspace_bytes(4096, 8, 256, 8) >= a
+    assert N.ep_workspace_bytes(0, 8, 256, 1) > 0
+    assert N.ep_workspace_bytes(10, 0, 4, 1) == 0           # K < 1
+    assert N.ep_workspace_bytes(10, 2, 6, 4) == 0           # E % R != 0
+    assert N.ep_workspace_bytes(10, 2, 5000, 1) == 0        # E too large
+    assert N.ep_workspace_bytes(-1, 2, 4, 1) == 0
+    assert N.ep_ec_workspace_bytes(8192, 64, 256) >= 64 * 256 * 4 + 8193 * 8
+    assert N.ep_ec_workspace_bytes(8, 0, 4) == 0
+
+
+A = 0x10000        # fake 256-aligned device address
+B = 0x20000
+WS = 0x100000
+
+
+def _layout(**kw):
+    args = dict(topk_idx=A, T=16, K=2, E=8, R=1, counts=A, offsets=A, tokens_per_rank=A,
+                is_token_in_rank=A, num_invalid=A, ws=WS, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return N.ep_get_dispatch_layout(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=0), N.EP_ERR_INVALID_ARG),
+    (dict(T=-1), N.EP_ERR_INVALID_ARG),
+    (dict(E=0), N.EP_ERR_INVALID_ARG),
+    (dict(E=4097), N.EP_ERR_UNSUPPORTED),
+    (dict(E=8, R=3), N.EP_ERR_INVALID_ARG),
+    (dict(R=2048, E=2048), N.EP_ERR_UNSUPPORTED),
+    (dict(counts=None), N.EP_ERR_INVALID_ARG),
+    (dict(offsets=None), N.EP_ERR_INVALID_ARG),
+    (dict(num_invalid=None), N.EP_ERR_INVALID_ARG),
+    (dict(topk_idx=None), N.EP_ERR_INVALID_ARG),
+    (dict(topk_idx=A + 2), N.EP_ERR_INVALID_ARG),
+    (dict(ws=None), N.EP_ERR_WORKSPACE),
+    (dict(ws=WS + 16), N.EP_ERR_WORKSPACE),
+    (dict(ws_bytes=16), N.EP_ERR_WORKSPACE),
+    (dict(T=1 << 30, K=4), N.EP_ERR_INVALID_ARG),
+])
+def test_layout_rejects(kw, status):
+    assert _layout(**kw) == status
+
+
+def _dispatch(**kw):
+    args = dict(x=A, T=16, H=256, topk_idx=A, K=2, E=8, offsets=A, layout=0, cap_or_max_rows=32,
+                quant=0, recv_x=B, recv_scales=None, slot=A, recv_src=A, num_dropped=A, ws=WS,
+                ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return N.ep_dispatch(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=12), N.EP_ERR_INVALID_ARG),
+    (dict(H=0), N.EP_ERR_INVALID_ARG),
+    (dict(quant=1, H=200, recv_scales=A), N.EP_ERR_INVALID_ARG),     # fp8 needs H % 128 == 0
+    (dict(quant=1, recv_scales=None), N.EP_ERR_INVALID_ARG),
+    (dict(quant=7), N.EP_ERR_INVALID_ARG),
+    (dict(layout=5), N.EP_ERR_INVALID_ARG),
+    (dict(cap_or_max_rows=-1), N.EP_ERR_INVALID_ARG),
+    (dict(layout=1, E=4096, cap_or_max_rows=1 << 20), N.EP_ERR_INVALID_ARG),   # E*cap >= 2^31
+    (dict(x=A + 8), N.EP_ERR_INVALID_ARG),                          # 16-byte alignment
+    (dict(recv_x=B + 4), N.EP_ERR_INVALID_ARG),
+    (dict(x=None), N.EP_ERR_INVALID_ARG),
+    (dict(recv_x=None), N.EP_ERR_INVALID_ARG),
+    (dict(slot=None), N.EP_ERR_INVALID_ARG),
+    (dict(offsets=None), N.EP_ERR_INVALID_ARG),
+    (dict(num_dropped=None), N.EP_ERR_INVALID_ARG),
+    (dict(K=0), N.EP_ERR_INVALID_ARG),
+    (dict(E=9000), N.EP_ERR_UNSUPPORTED),
+    (dict(ws=None), N.EP_ERR_WORKSPACE),
+    (dict(ws_bytes=100), N.EP_ERR_WORKSPACE),
+])
+def test_dispatch_rejects(kw, status):
+    assert _dispatch(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=4), N.EP_ERR_INVALID_ARG),
+    (dict(H=20), N.EP_ERR_INVALID_ARG),
+    (dict(K=0), N.EP_ERR_INVALID_ARG),
+    (dict(T=-3), N.EP_ERR_INVALID_ARG),
+    (dict(y=None), N.EP_ERR_INVALID_ARG),
+    (dict(y_rows=-1), N.EP_ERR_INVALID_ARG),
+    (dict(out=None), N.EP_ERR_INVALID_ARG),
+    (dict(slot=None), N.EP_ERR_INVALID_ARG),
+    (dict(out=B + 8), N.EP_ERR_INVALID_ARG),
+    (dict(topk_weights=A + 1), N.EP_ERR_INVALID_ARG),
+])
+def test_combine_rejects(kw, status):
+    args = dict(y=A, y_rows=32, H=256, slot=A, topk_weights=None, T=16, K=2, out=B, stream=None)
+    args.update(kw)
+    assert N.ep_combine(**args, check=False) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=0), N.EP_ERR_INVALID_ARG),
+    (dict(C=0), N.EP_ERR_INVALID_ARG),
+    (dict(H=10), N.EP_ERR_INVALID_ARG),
+    (dict(T=-1), N.EP_ERR_INVALID_ARG),
+    (dict(token_indices=None), N.EP_ERR_INVALID_ARG),
+    (dict(recv_x=None), N.EP_ERR_INVALID_ARG),
+    (dict(tok_off=None), N.EP_ERR_INVALID_ARG),
+    (dict(tok_ent=None), N.EP_ERR_INVALID_ARG),
+    (dict(num_invalid=None), N.EP_ERR_INVALID_ARG),
+    (dict(x=A + 4), N.EP_ERR_INVALID_ARG),
+    (dict(ws=None), N.EP_ERR_WORKSPACE),
+    (dict(ws_bytes=64), N.EP_ERR_WORKSPACE),
+    (dict(E=1 << 16, C=1 << 16), N.EP_ERR_INVALID_ARG),
+])
+def test_ec_dispatch_rejects(kw, status):
+    args = dict(x=A, T=16, H=64, token_indices=A, E=4, C=8, recv_x=B, tok_off=A, tok_ent=A,
+                num_invalid=A, ws=WS, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    assert N.ep_dispatch_expert_choice(**args, check=False) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=0), N.EP_ERR_INVALID_ARG),
+    (dict(H=12), N.EP_ERR_INVALID_ARG),
+    (dict(weights=None), N.EP_ERR_INVALID_ARG),
+    (dict(tok_off=None), N.EP_ERR_INVALID_ARG),
+    (dict(out=B + 2), N.EP_ERR_INVALID_ARG),
+])
+def test_ec_combine_rejects(kw, status):
+    args = dict(y=A, weights=A, E=4, C=8, H=64, tok_off=A, tok_ent=A, T=16, out=B, stream=None)
+    args.update(kw)
+    assert N.ep_combine_expert_choice(**args, check=False) == status
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(N.EpError):
+        N.ep_combine(A, 32, 12, A, None, 16, 2, B, None)
