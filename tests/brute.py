@@ -162,3 +162,15 @@ def ec_invert(token_indices, T):
     ent = j[order].astype(np.int32)
     off = np.concatenate([[0], np.cumsum(np.bincount(flat[j], minlength=T))]).astype(np.int32)
     return off, ent
+
+
+def multiplicity_times_x(x_bits, m):
+    """bf16(m_t * x_t) per row, where a zero result is +0: the sum starts
+    from +0, and +0 + (-0) = +0, so neither a token nobody received nor a
+    sum of -0 terms gives -0.  m_t * x_t is exact in fp32 for m_t <= 2^16;
+    numpy forms it and torch's cast rounds it to bf16."""
+    import torch
+    xf = (np.asarray(x_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    prod = (xf * np.asarray(m, np.float32)[:, None]).astype(np.float32)
+    prod = np.where(prod == 0, np.float32(0.0), prod)
+    return torch.from_numpy(np.ascontiguousarray(prod)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)

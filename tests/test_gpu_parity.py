@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import brute
 import golden_io
 import gpu_util as G
 import oracle
@@ -149,7 +150,7 @@ def test_dispatch_empty_and_all_padding():
     (3, 128, 2, 1, "contiguous", None),
     (77, 384, 10, 3, "padded", 4),
     (300, 7168, 64, 8, "contiguous", None),
-    (129, 1280, 256, 8, "padded", 128),     # 160 pieces: two 128-channel groups per 16 lanes... per block
+    (129, 1280, 256, 8, "padded", 128),     # 10 groups per row
 ])
 def test_dispatch_fp8_parity(T, H, E, K, lay, cap):
     _announce(f"dispatch fp8 T={T} H={H} E={E} K={K} {lay}")
@@ -192,11 +193,10 @@ def test_dispatch_fp8_golden_group():
 
 
 def test_fp8_every_e4m3_boundary():
-    """Rows built so that x / s lands exactly on every e4m3 value, every
-    midpoint and one fp32 ulp either side (s = 2^k so the division is exact
-    scaling): the GPU codes must equal the oracle's."""
+    """A row built so that x / s lands exactly on every e4m3 value, every
+    midpoint, and one bf16 step either side (s = 2^-4, so the division is an
+    exact scaling): the GPU codes must equal the oracle's."""
     _announce("fp8 boundaries")
-    import brute
     tab = brute.e4m3_table()
     pos = np.sort(tab[:127][~np.isnan(tab[:127])])
     mids = (pos[:-1] + pos[1:]) / 2
@@ -256,9 +256,8 @@ def test_combine_unit_weights_round_trip_exact():
     recv, _, slot, _, _ = G.dispatch(x_d, idx_d, c.E, L)
     out = G.combine(recv, slot, None)
     torch.cuda.synchronize()
-    m = (c.topk_idx >= 0).sum(axis=1).astype(np.float32)
-    ref = W.bf16_bits(W.bf16_to_f32(c.x) * m[:, None])
-    assert np.array_equal(G.host(out), ref)
+    m = (c.topk_idx >= 0).sum(axis=1)
+    assert np.array_equal(G.host(out), brute.multiplicity_times_x(c.x, m))
 
 
 # ---------------------------------------------------------------- expert choice
@@ -306,8 +305,9 @@ def test_expert_choice_round_trip_exact():
     out = G.ec_combine(recv, ones, off, ent, c.T)
     torch.cuda.synchronize()
     flat = c.token_indices.ravel()
-    m = np.bincount(flat[flat >= 0], minlength=c.T).astype(np.float32)
-    assert np.array_equal(G.host(out), W.bf16_bits(W.bf16_to_f32(c.x) * m[:, None]))
+    m = np.bincount(flat[flat >= 0], minlength=c.T)
+    assert (m == 0).any() and (m > 32).any()
+    assert np.array_equal(G.host(out), brute.multiplicity_times_x(c.x, m))
 
 
 # ---------------------------------------------------------------- the named workloads
@@ -335,7 +335,6 @@ def _token_choice_full(c, sample_tokens=256, sample_rows=64):
         assert np.array_equal(G.host(recv[torch.from_numpy(wr).to(G.DEV).long()]), q_ref[wr])
         assert np.array_equal(G.host(sc)[wr], sc_ref[wr])
         # y = dequantised rows (identity expert), built on the host from the oracle's codes
-        import brute
         tab = brute.e4m3_table().astype(np.float32)
         y = np.zeros((rows, c.H), np.uint16)
         deq = tab[q_ref[wr]] * np.repeat(sc_ref[wr], 128, axis=1)
@@ -368,7 +367,8 @@ def _token_choice_full(c, sample_tokens=256, sample_rows=64):
     if not fp8:
         # size-free exact pin: unit weights over y = dispatch(x) gives bf16(m x)
         m = torch.from_numpy((s_ref >= 0).sum(axis=1).astype(np.float32)).to(G.DEV)
-        exp = (x_d.float() * m[:, None]).to(torch.bfloat16)
+        prod = x_d.float() * m[:, None]
+        exp = torch.where(prod == 0, 0.0, prod).to(torch.bfloat16)      # sums start from +0
         assert torch.equal(out1.view(torch.int16), exp.view(torch.int16))
 
 
@@ -411,8 +411,8 @@ def test_workload_expert_choice():
     torch.cuda.synchronize()
     G.assert_combine_close(G.host(out), oracle.ec_combine(recv_ref, c.weights, c.token_indices, c.T))
     flat = c.token_indices.ravel()
-    m = np.bincount(flat, minlength=c.T).astype(np.float32)
-    assert np.array_equal(G.host(out1), W.bf16_bits(W.bf16_to_f32(c.x) * m[:, None]))
+    m = np.bincount(flat, minlength=c.T)
+    assert np.array_equal(G.host(out1), brute.multiplicity_times_x(c.x, m))
 
 
 def test_determinism_prefill():

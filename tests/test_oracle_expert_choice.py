@@ -68,14 +68,13 @@ def test_expert_choice_workload_shape():
 def test_ec_combine_unit_weight_round_trip():
     """Unit weights with y = dispatch(x): out[t] = bf16(m_t * x_t), m_t = number
     of entries that picked t (up to 64 here); unpicked tokens -> +0."""
-    c = W.random_expert_choice(8, 120, 32, 48, 20, p_empty=0.1, hot=6)
+    c = W.random_expert_choice(8, 400, 32, 48, 20, p_empty=0.1, hot=6)
     recv, _ = oracle.ec_dispatch(c.x, c.token_indices)
     out = oracle.ec_combine(recv, np.ones((c.E, c.C), np.float32), c.token_indices, c.T)
     flat = c.token_indices.ravel()
-    m = np.bincount(flat[flat >= 0], minlength=c.T).astype(np.float32)
-    assert m.max() >= 40
-    ref = W.bf16_bits(W.bf16_to_f32(c.x) * m[:, None])
-    assert np.array_equal(out, ref)
+    m = np.bincount(flat[flat >= 0], minlength=c.T)
+    assert m.max() >= 40 and (m == 0).any()
+    assert np.array_equal(out, brute.multiplicity_times_x(c.x, m))
     assert (out[m == 0] == 0).all()
 
 
