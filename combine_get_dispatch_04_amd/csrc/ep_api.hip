@@ -12,6 +12,7 @@ namespace {
 
 constexpr int kMaxExperts = 4096;   // the layout keeps per-expert counts in LDS
 constexpr int kMaxRanks = 1024;
+constexpr int kMaxTopk = 1024;      // a chunk of the layout holds at least one token's row
 constexpr int64_t kI32 = 2147483647LL;
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -22,7 +23,7 @@ ep_status_t check_layout_sizes(int T, int K, int E, int R)
 {
     if (T < 0 || K < 1 || E < 1 || R < 1)
         return EP_ERR_INVALID_ARG;
-    if (E > kMaxExperts || R > kMaxRanks)
+    if (E > kMaxExperts || R > kMaxRanks || K > kMaxTopk)
         return EP_ERR_UNSUPPORTED;
     if (E % R != 0)
         return EP_ERR_INVALID_ARG;

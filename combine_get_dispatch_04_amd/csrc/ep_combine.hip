@@ -10,7 +10,7 @@
 // One block per (token, row segment); each thread owns PPT 16-byte pieces
 // (8 channels each) and keeps 8*PPT fp32 accumulators.  For every source row
 // (block-uniform, so the row index and the weight are scalar loads) it loads
-// its pieces with non-temporal loads (each y row is read once) and
+// its pieces with non-temporal buffer loads (each y row is read once) and
 // accumulates with fp32 FMAs in ascending k / entry order, then rounds once
 // to bf16 (nearest even).  A token with no source row writes +0.
 #include "ep_common.h"
@@ -24,12 +24,11 @@ template <int PPT>
 __device__ __forceinline__ void acc_row(float (&acc)[PPT][8], const char *src, float wk, int seg0,
                                         int pieces)
 {
+    const rsrc_t row = row_rsrc(src, pieces * 16);     // pieces past the row read as zero
     u32x4 v[PPT];
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-        int i = seg0 + threadIdx.x + j * blockDim.x;
-        v[j] = i < pieces ? ld16_nt(src + (size_t)i * 16) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int j = 0; j < PPT; ++j)
+        v[j] = row_ld16(row, (seg0 + threadIdx.x + j * blockDim.x) * 16);
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
         acc[j][0] = fmaf(wk, bf16_lo(v[j].x), acc[j][0]);

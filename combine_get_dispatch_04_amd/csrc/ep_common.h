@@ -30,6 +30,35 @@ __device__ __forceinline__ void st8_nt(void *p, u32x2 v)
     __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
 }
 
+// Buffer (V#) accesses with an explicit cache policy.  A descriptor covers
+// one row (base = the row, num_records = its bytes), so pieces past the row
+// end read as zero and are not written.  Policy bits of gfx950 buffer
+// instructions: bit 0 = sc0, bit 1 = nt, bit 4 = sc1.  Measured on the
+// prefill workload: receive-row stores with sc1 and row loads with nt were
+// the fastest of the eight combinations each (dispatch 80 vs 95 us with nt
+// stores; combine 93 vs 147 us with plain loads).
+constexpr int kBufferDword3 = 0x00020000;     // raw 32-bit data format
+constexpr int kStorePolicy = 16;              // sc1
+constexpr int kLoadPolicy = 2;                // nt
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t row_rsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, kBufferDword3);
+}
+__device__ __forceinline__ void row_st16(rsrc_t r, int off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStorePolicy);
+}
+__device__ __forceinline__ void row_st8(rsrc_t r, int off, u32x2 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStorePolicy);
+}
+__device__ __forceinline__ u32x4 row_ld16(rsrc_t r, int off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy);
+}
+
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -76,6 +105,12 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 __device__ __forceinline__ uint64_t lanemask_lt(int lane)
 {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+// Number of set bits of m in lanes below mine (mbcnt).
+__device__ __forceinline__ int lanes_below(uint64_t m)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Lanes of this wave whose `key` equals mine, among lanes where `active`

@@ -6,7 +6,7 @@
 // Token-major: one block per (token, row segment).  The block reads its
 // piece of x[t] once into registers (16 bytes per thread per piece), then
 // for each of the token's K slots computes the receive row from the layout
-// tables and stores the piece there.  The slot arithmetic reads only
+// tables and stores the piece there (buffer stores bounded by the row).  The slot arithmetic reads only
 // block-uniform addresses, so it runs on the scalar unit.  fp8 quantises
 // once per token: a 128-channel group is 16 consecutive lanes; its |max| is
 // reduced across them with lane shuffles, the scale is a correctly rounded
@@ -52,7 +52,7 @@ template <int PPT, bool FP8>
 __global__ void __launch_bounds__(256)
 dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict__ topk_idx, int K,
                 int E, const int32_t *__restrict__ offsets, int padded, int cap_or_rows, int CT,
-                const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ local_rank,
+                int nchunk, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ local_rank,
                 void *__restrict__ recv_x, float *__restrict__ recv_s,
                 int32_t *__restrict__ slot_out, int32_t *__restrict__ recv_src,
                 int32_t *__restrict__ num_dropped)
@@ -115,7 +115,7 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
         const int e = trow[k];
         int s = -1;
         if ((unsigned)e < (unsigned)E) {
-            const int r = chunk_base[(int64_t)c * E + e] + rrow[k];
+            const int r = chunk_base[(int64_t)e * nchunk + c] + rrow[k];
             if (padded)
                 s = r < cap_or_rows ? e * cap_or_rows + r : -1;
             else {
@@ -132,25 +132,20 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
         if (s < 0)
             continue;
         if constexpr (FP8) {
-            char *dst = reinterpret_cast<char *>(recv_x) + (size_t)s * H;
+            const rsrc_t dst = row_rsrc(reinterpret_cast<char *>(recv_x) + (size_t)s * H, H);
             float *sdst = recv_s + (size_t)s * G;
 #pragma unroll
             for (int j = 0; j < PPT; ++j) {
                 int i = seg0 + tid + j * bd;
-                if (i < pieces) {
-                    st8_nt(dst + (size_t)i * 8, q[j]);
-                    if ((tid & 15) == 0)
-                        sdst[i >> 4] = sc[j];
-                }
+                row_st8(dst, i * 8, q[j]);
+                if ((tid & 15) == 0 && i < pieces)
+                    sdst[i >> 4] = sc[j];
             }
         } else {
-            char *dst = reinterpret_cast<char *>(recv_x) + (size_t)s * H * 2;
+            const rsrc_t dst = row_rsrc(reinterpret_cast<char *>(recv_x) + (size_t)s * H * 2, H * 2);
 #pragma unroll
-            for (int j = 0; j < PPT; ++j) {
-                int i = seg0 + tid + j * bd;
-                if (i < pieces)
-                    st16_nt(dst + (size_t)i * 16, v[j]);
-            }
+            for (int j = 0; j < PPT; ++j)
+                row_st16(dst, (seg0 + tid + j * bd) * 16, v[j]);
         }
     }
 }
@@ -195,7 +190,8 @@ hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint
 #define EP_DISPATCH_CASE(N)                                                                     \
     case N:                                                                                     \
         hipLaunchKernelGGL((dispatch_kernel<N, FP8>), grid, block, 0, s, x, H, topk_idx, p.K, \
-                           p.E, offsets, padded, cap_or_rows, p.CT, hist, rank, recv_x, recv_s, \
+                           p.E, offsets, padded, cap_or_rows, p.CT, p.nchunk, hist, rank,      \
+                           recv_x, recv_s,                                                      \
                            slot, recv_src, num_dropped);                                        \
         break;
     switch (rs.ppt) {

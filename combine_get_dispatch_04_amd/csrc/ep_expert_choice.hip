@@ -125,13 +125,10 @@ ec_sort_copy_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__rest
     }
     for (int a = 0; a < n; ++a) {
         const int e = tmp[b + a];
-        char *dst = reinterpret_cast<char *>(recv) + (size_t)e * H * 2;
+        const rsrc_t dst = row_rsrc(reinterpret_cast<char *>(recv) + (size_t)e * H * 2, H * 2);
 #pragma unroll
-        for (int j = 0; j < PPT; ++j) {
-            int i = seg0 + tid + j * bd;
-            if (i < pieces)
-                st16_nt(dst + (size_t)i * 16, v[j]);
-        }
+        for (int j = 0; j < PPT; ++j)
+            row_st16(dst, (seg0 + tid + j * bd) * 16, v[j]);
     }
 
     if (blockIdx.y != 0)

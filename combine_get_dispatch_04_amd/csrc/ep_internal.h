@@ -14,6 +14,7 @@ struct LayoutPlan {
     int CT;        // tokens per chunk
     int nchunk;    // ceil(T / CT)
     int waves;     // waves per chunk block
+    int epl;       // entries per lane (1..32, a power of two)
     int nbits;     // bits needed for an expert id in [0, E)
     size_t lds;    // dynamic shared memory of the chunk kernel
     // workspace carve-up (byte offsets, 256-aligned)

@@ -13,7 +13,9 @@
 // rank among the chunk's entries of its expert, and writes the chunk's
 // histogram.  The scan kernel turns the chunk histograms into per-chunk
 // bases (column prefix over chunks) and the per-expert totals into counts
-// and offsets.  ep_dispatch later places entry (t,k) of expert e at
+// and offsets; when all of topk_idx fits one block (up to 16 waves x 64
+// lanes x 8 entries), that block does this itself and there is one launch.
+// ep_dispatch later places entry (t,k) of expert e at
 // offsets[e] + chunk_base[t / CT][e] + local_rank[t, k].
 #include "ep_common.h"
 #include "ep_internal.h"
@@ -22,10 +24,13 @@ namespace ep {
 
 namespace {
 
-constexpr int kEntriesPerLane = 8;   // target entries per lane and chunk
 constexpr int kMaxWaves = 16;
 constexpr int kLdsInts = 16384;      // 64 KiB per block
 constexpr int kMaxRanks = 1024;
+constexpr int kEpl = 8;              // entries per lane of a wave's run (at most)
+constexpr long long kTargetChunks = 32;
+constexpr int kScanSeg = 256;        // chunks per column segment in the scan
+constexpr int kScanTileInts = 16384 - 4096 - 32;
 
 // Offsets from per-expert totals held in shared memory: an exclusive scan
 // over E by the whole block.  Each thread owns a run of consecutive experts.
@@ -46,28 +51,54 @@ __device__ void offsets_from_totals(const int32_t *tot, int E, int32_t *offsets,
         offsets[E] = total;
 }
 
+// One block per chunk of CT tokens (n = CT*K entries <= waves*64*epl).  The
+// chunk's entries are staged in shared memory; wave w walks entries
+// [w*64*epl, (w+1)*64*epl) 64 at a time.  The kernels are short-lived and
+// each CU runs them from a cold instruction cache, so the loops are kept
+// compact (not unrolled) and their state lives in shared memory.
 __global__ void __launch_bounds__(1024)
 layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, int R, int CT,
-                    int nbits, int32_t *__restrict__ chunk_hist, int32_t *__restrict__ local_rank,
-                    int32_t *__restrict__ rank_part, int32_t *__restrict__ inval_part,
-                    uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ counts,
-                    int32_t *__restrict__ offsets, int32_t *__restrict__ tokens_per_rank,
-                    int32_t *__restrict__ num_invalid)
+                    int nbits, int epl, int32_t *__restrict__ chunk_hist,
+                    int32_t *__restrict__ local_rank, int32_t *__restrict__ rank_part,
+                    int32_t *__restrict__ inval_part, uint8_t *__restrict__ is_token_in_rank,
+                    int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                    int32_t *__restrict__ tokens_per_rank, int32_t *__restrict__ num_invalid)
 {
     extern __shared__ int32_t lds[];
     const int waves = blockDim.x / kWave;
+    const int nchunk = gridDim.x;
+    const int per_wave = kWave * epl;                  // a power of two
+    const int wave_shift = 31 - __builtin_clz(per_wave);
+    const int cap = waves * per_wave;
     int32_t *whist = lds;                 // [waves][E] running counts, then per-wave bases
     int32_t *tot = whist + waves * E;     // [E] chunk totals
     int32_t *rcnt = tot + E;              // [R] tokens per rank in this chunk
     int32_t *tmp = rcnt + R;              // [32] scratch
+    int32_t *ent = tmp + 32;              // [cap] the chunk's entries
+    int32_t *rkl = ent + cap;             // [cap] rank inside the owning wave's run
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int chunk = blockIdx.x;
-    const bool single = gridDim.x == 1;
+    const bool single = nchunk == 1;
     const int t0 = chunk * CT;
     const int t1 = min(T, t0 + CT);
     const int64_t base = (int64_t)t0 * K;
     const int n = (t1 - t0) * K;
 
+    // ---- stage the entries: 8 loads in flight per thread
+    for (int i0 = 0; i0 < n; i0 += blockDim.x * 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * blockDim.x + tid;
+            v[u] = i < n ? topk_idx[base + i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * blockDim.x + tid;
+            if (i < n)
+                ent[i] = v[u];
+        }
+    }
     for (int i = tid; i < waves * E; i += blockDim.x)
         whist[i] = 0;
     for (int i = tid; i < R; i += blockDim.x)
@@ -76,93 +107,91 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
         tmp[tid] = 0;
     __syncthreads();
 
-    // ---- pass 1: per-wave stable ranks
-    const int span = (((n + waves - 1) / waves) + kWave - 1) & ~(kWave - 1);
-    const int lo = min(n, w * span), hi = min(n, lo + span);
+    // ---- stable ranks inside the wave's run: running count + same-expert lanes below
     int32_t *myh = whist + w * E;
+    const int lo = w * per_wave, hi = min(n, lo + per_wave);
     int inval = 0;
+#pragma unroll 1
     for (int s0 = lo; s0 < hi; s0 += kWave) {
         const int i = s0 + lane;
-        const bool in = i < hi;
-        const int e = in ? topk_idx[base + i] : -1;
-        const bool ok = in && (unsigned)e < (unsigned)E;
-        inval += (in && e != -1 && !ok) ? 1 : 0;
+        const int e = i < hi ? ent[i] : -1;
+        const bool ok = (unsigned)e < (unsigned)E;
+        inval += (e != -1 && !ok) ? 1 : 0;
         const uint64_t peers = match_key(e, ok, nbits);
         if (ok) {
             const int r0 = myh[e];
-            const int below = __popcll(peers & lanemask_lt(lane));
-            if ((peers >> lane) == 1ull)         // highest lane of the group
+            if ((peers >> lane) == 1ull)           // highest lane of the group publishes
                 myh[e] = r0 + __popcll(peers);
-            local_rank[base + i] = r0 + below;
+            rkl[i] = r0 + lanes_below(peers);
         }
     }
     __syncthreads();
 
     // ---- per-wave bases (prefix over waves) and chunk totals
-    for (int e = tid; e < E; e += blockDim.x) {
+    for (int x = tid; x < E; x += blockDim.x) {
         int run = 0;
         for (int ww = 0; ww < waves; ++ww) {
-            int h = whist[ww * E + e];
-            whist[ww * E + e] = run;
+            int h = whist[ww * E + x];
+            whist[ww * E + x] = run;
             run += h;
         }
-        tot[e] = run;
-        chunk_hist[(int64_t)chunk * E + e] = single ? 0 : run;
+        tot[x] = run;
+        chunk_hist[(int64_t)x * nchunk + chunk] = single ? 0 : run;
         if (single)
-            counts[e] = run;
+            counts[x] = run;
     }
     __syncthreads();
-
-    // ---- pass 2: add the wave's base to its entries' ranks
-    if (w > 0) {
-        for (int s0 = lo; s0 < hi; s0 += kWave) {
-            const int i = s0 + lane;
-            if (i < hi) {
-                const int e = topk_idx[base + i];
-                if ((unsigned)e < (unsigned)E)
-                    local_rank[base + i] += myh[e];
-            }
-        }
+    for (int i = tid; i < n; i += blockDim.x) {
+        const int e = ent[i];
+        if ((unsigned)e < (unsigned)E)
+            local_rank[base + i] = rkl[i] + whist[(i >> wave_shift) * E + e];
     }
 
-    // ---- ranks: is_token_in_rank rows and per-chunk tokens_per_rank
+    // ---- ranks: is_token_in_rank rows and this chunk's tokens_per_rank
     const int per_rank = E / R;
-    for (int t = t0 + tid; t < t1; t += blockDim.x) {
-        const int32_t *row = topk_idx + (int64_t)t * K;
-        if (R <= 64) {
+    const int ntok = t1 - t0;
+    if (R <= 64) {
+        for (int tb = 0; tb < ntok; tb += blockDim.x) {    // same trip count for every lane
+            const int tl = tb + tid;
             uint64_t m = 0;
-            for (int k = 0; k < K; ++k) {
-                int e = row[k];
-                if ((unsigned)e < (unsigned)E)
-                    m |= 1ull << (e / per_rank);
+            if (tl < ntok) {
+                const int32_t *row = ent + tl * K;
+                for (int k = 0; k < K; ++k) {
+                    const int ee = row[k];
+                    if ((unsigned)ee < (unsigned)E)
+                        m |= 1ull << (R == 1 ? 0 : ee / per_rank);
+                }
+                if (is_token_in_rank)
+                    for (int r = 0; r < R; ++r)
+                        is_token_in_rank[(int64_t)(t0 + tl) * R + r] = (uint8_t)((m >> r) & 1u);
             }
+            for (int r = 0; r < R; ++r) {
+                const int c = __popcll(ballot((m >> r) & 1u));
+                if (lane == 0 && c)
+                    atomicAdd(&rcnt[r], c);
+            }
+        }
+    } else {
+        for (int tl = tid; tl < ntok; tl += blockDim.x) {
+            const int32_t *row = ent + tl * K;
             if (is_token_in_rank)
                 for (int r = 0; r < R; ++r)
-                    is_token_in_rank[(int64_t)t * R + r] = (uint8_t)((m >> r) & 1u);
-            while (m) {
-                int r = __ffsll((unsigned long long)m) - 1;
-                atomicAdd(&rcnt[r], 1);
-                m &= m - 1;
-            }
-        } else {
-            if (is_token_in_rank)
-                for (int r = 0; r < R; ++r)
-                    is_token_in_rank[(int64_t)t * R + r] = 0;
+                    is_token_in_rank[(int64_t)(t0 + tl) * R + r] = 0;
             for (int k = 0; k < K; ++k) {
-                int e = row[k];
-                if ((unsigned)e >= (unsigned)E)
+                const int ee = row[k];
+                if ((unsigned)ee >= (unsigned)E)
                     continue;
-                int r = e / per_rank;
+                const int r = ee / per_rank;
                 bool first = true;
                 for (int k2 = 0; k2 < k && first; ++k2) {
-                    int e2 = row[k2];
+                    const int e2 = row[k2];
                     if ((unsigned)e2 < (unsigned)E && e2 / per_rank == r)
                         first = false;
                 }
                 if (first) {
                     atomicAdd(&rcnt[r], 1);
                     if (is_token_in_rank)
-                        is_token_in_rank[(int64_t)t * R + r] = 1;
+                        is_token_in_rank[(int64_t)(t0 + tl) * R + r] = 1;
                 }
             }
         }
@@ -182,59 +211,97 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
         offsets_from_totals(tot, E, offsets, tmp);
     } else {
         for (int r = tid; r < R; r += blockDim.x)
-            rank_part[(int64_t)chunk * R + r] = rcnt[r];
+            rank_part[(int64_t)r * nchunk + chunk] = rcnt[r];
         if (tid == 0)
             inval_part[chunk] = tmp[31];
     }
 }
 
-// Column prefix over chunks: chunk_hist[c][e] becomes the number of entries
-// of expert e in chunks before c; totals give counts and offsets.
+// Column prefix over chunks.  The chunk tables are column-major
+// ([column][chunk]): columns 0..E-1 are the expert histograms (rewritten in
+// place with their exclusive prefix over chunks, i.e. the chunk bases, and
+// summed into counts), columns E..E+R-1 the per-rank token counts and the
+// last the invalid-entry counts (only summed).  The tables are contiguous,
+// so tiles of (columns x chunks) are copied into shared memory with
+// coalesced loads, one thread scans one column of the tile sequentially
+// (rows padded by one int against bank conflicts), and the expert columns
+// are copied back coalesced.  Columns longer than a tile are done in
+// segments with the running sum kept in the column's thread.
 __global__ void __launch_bounds__(1024)
 layout_scan_kernel(int nchunk, int E, int R, int32_t *__restrict__ chunk_hist,
                    const int32_t *__restrict__ rank_part, const int32_t *__restrict__ inval_part,
                    int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                    int32_t *__restrict__ tokens_per_rank, int32_t *__restrict__ num_invalid)
 {
-    __shared__ int32_t tot[4096];
-    __shared__ int tmp[32];
-    const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += blockDim.x) {
-        int run = 0;
-        int c = 0;
-        for (; c + 8 <= nchunk; c += 8) {
-            int h[8];
+    extern __shared__ int32_t sm[];
+    const int tid = threadIdx.x, bd = blockDim.x;
+    const int ncol = E + R + 1;
+    // a segment of a column holds up to `seg` chunks, seg a power of two so
+    // that an element index splits into (column, chunk) by shift and mask
+    int sh = 0;
+    while ((1 << sh) < nchunk && (1 << sh) < kScanSeg)
+        ++sh;
+    const int seg = 1 << sh;
+    const int ld = seg + 1;                       // odd row stride: no bank conflicts
+    int cpt = kScanTileInts / ld;                 // columns per tile
+    cpt = cpt < 1 ? 1 : (cpt > bd ? bd : cpt);
+    int32_t *tile = sm;
+    int32_t *tot = sm + kScanTileInts;            // [E]
+    int *tmp = tot + E;                           // [32]
+    for (int col0 = 0; col0 < ncol; col0 += cpt) {
+        const int nc = min(cpt, ncol - col0);
+        const int cnt = nc << sh;
+        int carry = 0;                            // running sum of column col0 + tid
+        for (int s0 = 0; s0 < nchunk; s0 += seg) {
+            const int sl = min(seg, nchunk - s0);
+            for (int q0 = 0; q0 < cnt; q0 += 8 * bd) {
+                int v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                h[u] = chunk_hist[(int64_t)(c + u) * E + e];
+                for (int u = 0; u < 8; ++u) {
+                    const int q = q0 + u * bd + tid;
+                    const int cl = q >> sh, c = q & (seg - 1), col = col0 + cl;
+                    const int32_t *src = col < E       ? chunk_hist + (int64_t)col * nchunk
+                                         : col < E + R ? rank_part + (int64_t)(col - E) * nchunk
+                                                       : inval_part;
+                    v[u] = (q < cnt && c < sl) ? src[s0 + c] : 0;
+                }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                chunk_hist[(int64_t)(c + u) * E + e] = run;
-                run += h[u];
+                for (int u = 0; u < 8; ++u) {
+                    const int q = q0 + u * bd + tid;
+                    if (q < cnt)
+                        tile[(q >> sh) * ld + (q & (seg - 1))] = v[u];
+                }
+            }
+            __syncthreads();
+            if (tid < nc) {
+                int32_t *row = tile + tid * ld;
+                for (int c = 0; c < sl; ++c) {
+                    const int h = row[c];
+                    row[c] = carry;
+                    carry += h;
+                }
+            }
+            __syncthreads();
+            for (int q = tid; q < cnt; q += bd) {
+                const int cl = q >> sh, c = q & (seg - 1), col = col0 + cl;
+                if (col < E && c < sl)
+                    chunk_hist[(int64_t)col * nchunk + s0 + c] = tile[cl * ld + c];
+            }
+            __syncthreads();
+        }
+        if (tid < nc) {
+            const int col = col0 + tid;
+            if (col < E) {
+                tot[col] = carry;
+                counts[col] = carry;
+            } else if (col < E + R) {
+                if (tokens_per_rank)
+                    tokens_per_rank[col - E] = carry;
+            } else {
+                num_invalid[0] = carry;
             }
         }
-        for (; c < nchunk; ++c) {
-            int h = chunk_hist[(int64_t)c * E + e];
-            chunk_hist[(int64_t)c * E + e] = run;
-            run += h;
-        }
-        tot[e] = run;
-        counts[e] = run;
     }
-    if (tokens_per_rank)
-        for (int r = tid; r < R; r += blockDim.x) {
-            int s = 0;
-            for (int c = 0; c < nchunk; ++c)
-                s += rank_part[(int64_t)c * R + r];
-            tokens_per_rank[r] = s;
-        }
-    int inv = 0;
-    for (int c = tid; c < nchunk; c += blockDim.x)
-        inv += inval_part[c];
-    int tot_inv;
-    block_exclusive_scan(inv, tmp, &tot_inv);
-    if (tid == 0)
-        num_invalid[0] = tot_inv;
     __syncthreads();
     offsets_from_totals(tot, E, offsets, tmp);
 }
@@ -252,22 +319,50 @@ LayoutPlan make_layout_plan(int T, int K, int E, int R)
     while ((1 << p.nbits) < E)
         ++p.nbits;
     // The chunking must not depend on R: ep_dispatch re-derives it from
-    // (T, K, E) alone.  Shared memory is sized for the largest R.
-    int fit = (kLdsInts - E - kMaxRanks - 32) / E;
-    p.waves = fit < 1 ? 1 : (fit > kMaxWaves ? kMaxWaves : fit);
-    long long target = (long long)p.waves * kWave * kEntriesPerLane;
-    long long ct = target / K;
+    // (T, K, E) alone, so shared memory is sized for the largest R.  A wave
+    // with `epl` entries per lane stages and ranks 64 * epl entries (two
+    // ints each in shared memory, next to its E-entry histogram).
+    auto wmax_for = [&](int epl) {
+        int fit = (kLdsInts - E - kMaxRanks - 32) / (E + 2 * kWave * epl);
+        return fit < 1 ? 1 : (fit > kMaxWaves ? kMaxWaves : fit);
+    };
+    // A wave's 64-entry tiles form a dependent chain (shared-memory count,
+    // ballots, count update), so runs are kept short and spread over many
+    // waves.  An input that fits one block (some epl <= kEpl) takes one
+    // block, which also finishes the scan: one launch.  Otherwise: the
+    // fewest entries per lane that keep about kTargetChunks chunks.
+    const long long n = (long long)T * K;
+    long long cap = 0;
+    for (int epl = 1; epl <= kEpl; epl *= 2) {
+        const long long c = (long long)wmax_for(epl) * kWave * epl;
+        if (n <= c) {
+            p.epl = epl;
+            cap = c;
+            break;
+        }
+    }
+    if (cap == 0) {
+        p.epl = 1;
+        while (p.epl < kEpl && n > kTargetChunks * wmax_for(p.epl) * kWave * p.epl)
+            p.epl *= 2;
+        cap = (long long)wmax_for(p.epl) * kWave * p.epl;
+        while (cap < K && p.epl < kEpl) {   // a chunk holds at least one token
+            p.epl *= 2;
+            cap = (long long)wmax_for(p.epl) * kWave * p.epl;
+        }
+    }
+    const int wmax = wmax_for(p.epl);
+    long long ct = cap / K;
     if (ct < 1)
         ct = 1;
     if (ct > T && T > 0)
         ct = T;
     p.CT = (int)ct;
     p.nchunk = T > 0 ? (int)((T + ct - 1) / ct) : 0;
-    // no more waves than 64-entry tiles in a chunk
-    long long tiles = ((long long)p.CT * K + kWave - 1) / kWave;
-    if (tiles < p.waves)
-        p.waves = tiles < 1 ? 1 : (int)tiles;
-    p.lds = (size_t)(p.waves * E + E + R + 32) * sizeof(int32_t);
+    const long long per_wave = (long long)kWave * p.epl;
+    long long wv = ((long long)p.CT * K + per_wave - 1) / per_wave;
+    p.waves = wv < 1 ? 1 : (wv > wmax ? wmax : (int)wv);
+    p.lds = (size_t)(p.waves * E + E + R + 32 + 2 * p.waves * per_wave) * sizeof(int32_t);
     size_t off = 256;
     p.off_hist = off;
     off = align256(off + (size_t)p.nchunk * E * 4);
@@ -289,16 +384,20 @@ hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *
     int32_t *rank = reinterpret_cast<int32_t *>(ws + p.off_rank);
     int32_t *rpart = reinterpret_cast<int32_t *>(ws + p.off_rpart);
     int32_t *ipart = reinterpret_cast<int32_t *>(ws + p.off_ipart);
+    if ((long long)p.CT * p.K > (long long)p.waves * kWave * p.epl)
+        return hipErrorInvalidValue;     // a chunk's entries must fit its waves
     if (p.nchunk > 0) {
-        hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunk), dim3(p.waves * kWave), p.lds, s,
-                           topk_idx, p.T, p.K, p.E, p.R, p.CT, p.nbits, hist, rank, rpart, ipart,
-                           is_token_in_rank, counts, offsets, tokens_per_rank, num_invalid);
+hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunk), dim3(p.waves * kWave), p.lds, s,
+                           topk_idx, p.T, p.K, p.E, p.R, p.CT, p.nbits, p.epl, hist, rank, rpart,
+                           ipart, is_token_in_rank, counts, offsets, tokens_per_rank, num_invalid);
+
         hipError_t err = hipGetLastError();
         if (err != hipSuccess)
             return err;
     }
     if (p.nchunk != 1) {
-        hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(1024), 0, s, p.nchunk, p.E, p.R, hist,
+        hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(1024),
+                           (size_t)(kScanTileInts + p.E + 32) * sizeof(int32_t), s, p.nchunk, p.E, p.R, hist,
                            rpart, ipart, counts, offsets, tokens_per_rank, num_invalid);
         return hipGetLastError();
     }
