@@ -1,19 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE token dispatch/combine hot path on one MI355X.
 
-One step = ep_get_dispatch_layout + ep_dispatch (bf16, expert-contiguous
-receive buffer) + ep_combine (routing weights, identity experts: y = the
-receive buffer) on the prefill-shaped workload T=4096, H=7168, E=256, top-8
-with Zipf-skewed routing.  Inputs are seeded synthetic tensors, resident in
-HBM before the timed region.  W untimed warm-up steps, then exactly K timed
-steps between two device synchronisations; rank 0 prints one JSON line.
+Default workload (the headline metric): T=4096 tokens, H=7168, E=256
+experts, top-8 with Zipf-skewed routing.  One step = ep_get_dispatch_layout
++ ep_dispatch (bf16, expert-contiguous receive buffer) + ep_combine (routing
+weights, identity experts: y = the receive buffer).  Inputs are seeded
+synthetic tensors, resident in HBM before the timed region.  W untimed
+warm-up steps, then exactly K timed steps between two device
+synchronisations; one JSON line is printed.
+
+Other workloads (--workload): toy, decode (fp8 e4m3 with 128-channel scales
+into the padded [E, 128, H] buffer; combine reads bf16(q*s) rows made
+outside the timed region), expert_choice (ep_dispatch_expert_choice +
+ep_combine_expert_choice), large_padded.
 
 Also reported: per-operation times (HIP events on the stream the kernels run
-on, in a second pass after the timed region), the roofline of the dominant kernel (algorithmic bytes per launch over
-its average duration, against 8 TB/s), HBM traffic from the committed
-rocprofv3 counter summary when it was taken on the current kernel source,
-and the CPU oracle timed on the host on a bounded sample of the same
-workload.
+on, in a second pass after the timed region), the roofline of the dominant
+kernel (algorithmic bytes per launch over its average duration, against
+8 TB/s), HBM traffic from the committed rocprofv3 counter summary when it was
+taken on the current kernel sources, and the CPU oracle timed on the host on
+a bounded sample of the same workload.
 """
 import argparse
 import hashlib
@@ -27,9 +33,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "dispatch+combine tokens/s & achieved HBM GB/s, T=4096 H=7168 E=256 top-8"
 PEAK_HBM_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_T4096_H7168_E256_K8.json")
+HEADLINE_METRIC = "dispatch+combine tokens/s & achieved HBM GB/s, T=4096 H=7168 E=256 top-8"
 
 
 def kernel_source_hash():
@@ -41,11 +46,12 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def traffic_entry(kernel):
+def traffic_entry(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary,
     or None when that summary was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -55,6 +61,109 @@ def traffic_entry(kernel):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+# ----------------------------------------------------------------- paths
+class Path:
+    """A workload's hot path: named operations (each a list of libep calls on
+    one stream), the main kernel of each, and algorithmic bytes per op."""
+
+    def __init__(self, name, T, ops, kernel_of, alg_bytes, meta):
+        self.name, self.T, self.ops, self.kernel_of = name, T, ops, kernel_of
+        self.alg_bytes, self.meta = alg_bytes, meta
+
+
+def token_choice_path(c, N, torch, dev, sp):
+    T, H, E, K = c.T, c.H, c.E, c.K
+    fp8 = c.quant == "fp8_e4m3_g128"
+    padded = c.layout == "padded"
+    cap_or_rows = c.cap if padded else T * K
+    rows = E * c.cap if padded else T * K
+    P = lambda t: t.data_ptr() if t is not None else None
+    x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    idx = torch.from_numpy(c.topk_idx).to(dev)
+    w = torch.from_numpy(c.topk_weights).to(dev)
+    n_valid = int(((c.topk_idx >= 0) & (c.topk_idx < E)).sum())
+    ws_bytes = N.ep_workspace_bytes(T, K, E, 1)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    tpr = torch.empty(1, dtype=torch.int32, device=dev)
+    itr = torch.empty((T, 1), dtype=torch.uint8, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    recv = torch.empty((rows, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    scales = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+    slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+    src = torch.empty(rows, dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    quant = N.EP_QUANT_FP8_E4M3_G128 if fp8 else N.EP_QUANT_BF16
+    lay = N.EP_LAYOUT_PADDED if padded else N.EP_LAYOUT_CONTIGUOUS
+
+    def layout():
+        N.ep_get_dispatch_layout(P(idx), T, K, E, 1, P(counts), P(offsets), P(tpr), P(itr),
+                                 P(ninv), P(ws), ws_bytes, sp)
+
+    def dispatch():
+        N.ep_dispatch(P(x), T, H, P(idx), K, E, P(offsets), lay, cap_or_rows, quant, P(recv),
+                      P(scales), P(slot), P(src), P(nd), P(ws), ws_bytes, sp)
+
+    if fp8:
+        # identity expert on the dequantised rows, built once outside the timed region
+        layout()
+        dispatch()
+        torch.cuda.synchronize()
+        y = (recv.view(torch.float8_e4m3fn).float()
+             * scales.repeat_interleave(128, dim=1)).to(torch.bfloat16)
+        torch.cuda.synchronize()
+    else:
+        y = recv
+
+    def combine():
+        N.ep_combine(P(y), rows, H, P(slot), P(w), T, K, P(out), sp)
+
+    row_in = H + 4 * (H // 128) if fp8 else H * 2
+    alg = {"layout": T * K * 4,
+           "dispatch": T * H * 2 + n_valid * row_in + 2 * T * K * 4,
+           "combine": n_valid * H * 2 + T * H * 2 + 2 * T * K * 4}
+    kern = {"layout": "layout_chunk_kernel",
+            "dispatch": "dispatch_kernel", "combine": "combine_kernel"}
+    meta = {"T": T, "H": H, "E": E, "top_k": K, "recv_layout": c.layout, "quant": c.quant,
+            "cap": c.cap, "combine": "weighted", "valid_slots": n_valid}
+    return Path(c.name, T, [("layout", layout), ("dispatch", dispatch), ("combine", combine)],
+                kern, alg, meta)
+
+
+def expert_choice_path(c, N, torch, dev, sp):
+    T, H, E, C = c.T, c.H, c.E, c.C
+    P = lambda t: t.data_ptr()
+    x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    ti = torch.from_numpy(c.token_indices).to(dev)
+    w = torch.from_numpy(c.weights).to(dev)
+    ws_bytes = N.ep_ec_workspace_bytes(T, E, C)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    recv = torch.empty((E, C, H), dtype=torch.bfloat16, device=dev)
+    off = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    ent = torch.empty(E * C, dtype=torch.int32, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    flat = c.token_indices.ravel()
+    valid = flat[(flat >= 0) & (flat < T)]
+    n_valid, U = int(valid.size), int(np.unique(valid).size)
+
+    def dispatch():
+        N.ep_dispatch_expert_choice(P(x), T, H, P(ti), E, C, P(recv), P(off), P(ent), P(ninv),
+                                    P(ws), ws_bytes, sp)
+
+    def combine():
+        N.ep_combine_expert_choice(P(recv), P(w), E, C, H, P(off), P(ent), T, P(out), sp)
+
+    alg = {"dispatch": U * H * 2 + n_valid * H * 2 + E * C * 4 + (T + 1) * 4 + n_valid * 4,
+           "combine": n_valid * H * 2 + T * H * 2 + E * C * 4 + (T + 1) * 4 + n_valid * 4}
+    kern = {"dispatch": "ec_sort_copy_kernel", "combine": "ec_combine_kernel"}
+    meta = {"T": T, "H": H, "E": E, "capacity": C, "valid_entries": n_valid,
+            "distinct_tokens": U}
+    return Path(c.name, T, [("dispatch", dispatch), ("combine", combine)], kern, alg, meta)
+
+
 def cpu_baseline(c, budget_s):
     """The oracle as it stands (single thread) on full passes of the same
     workload until `budget_s` seconds have elapsed."""
@@ -62,17 +171,31 @@ def cpu_baseline(c, budget_s):
     reps = 0
     t0 = time.perf_counter()
     while True:
-        L = oracle.layout(c.topk_idx, c.E)
-        slot, _, _ = oracle.slots(c.topk_idx, c.E, False, c.T * c.K)
-        y = oracle.dispatch_bf16(c.x, slot, int(L["offsets"][-1]))
-        oracle.combine(y, slot, c.topk_weights)
+        if hasattr(c, "token_indices"):
+            recv, _ = oracle.ec_dispatch(c.x, c.token_indices)
+            oracle.ec_invert(c.token_indices, c.T)
+            oracle.ec_combine(recv, c.weights, c.token_indices, c.T)
+            what = "expert-choice dispatch, inverse map, weighted combine"
+        else:
+            padded = c.layout == "padded"
+            cap = c.cap if padded else c.T * c.K
+            rows = c.E * c.cap if padded else c.T * c.K
+            oracle.layout(c.topk_idx, c.E)
+            slot, _, _ = oracle.slots(c.topk_idx, c.E, padded, cap)
+            if c.quant == "fp8_e4m3_g128":
+                oracle.dispatch_fp8(c.x, slot, rows)
+                y = np.zeros((rows, c.H), np.uint16)
+            else:
+                y = oracle.dispatch_bf16(c.x, slot, rows)
+            oracle.combine(y, slot, c.topk_weights)
+            what = "layout, slots, dispatch, weighted combine"
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
     return {"value": reps * c.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full pass(es) of the same workload (layout, slots, bf16 dispatch, "
-                      f"weighted combine; {c.T} tokens each), {el:.1f} s on one host thread"}
+            "sample": f"{reps} full pass(es) of the same workload ({what}; {c.T} tokens each), "
+                      f"{el:.1f} s on one host thread"}
 
 
 def main():
@@ -80,10 +203,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "toy", "decode", "expert_choice", "large_padded"])
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write this many MiB of scratch before each step (cold caches)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the multi-GPU "
@@ -96,43 +223,28 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    c = W.prefill()
-    T, H, E, K = c.T, c.H, c.E, c.K
-    x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
-    idx = torch.from_numpy(c.topk_idx).to(dev)
-    w = torch.from_numpy(c.topk_weights).to(dev)
-    rows = T * K
-    N_valid = int((c.topk_idx >= 0).sum())
-    ws_bytes = N.ep_workspace_bytes(T, K, E, 1)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    tpr = torch.empty(1, dtype=torch.int32, device=dev)
-    itr = torch.empty((T, 1), dtype=torch.uint8, device=dev)
-    ninv = torch.empty(1, dtype=torch.int32, device=dev)
-    recv = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
-    slot = torch.empty((T, K), dtype=torch.int32, device=dev)
-    src = torch.empty(rows, dtype=torch.int32, device=dev)
-    nd = torch.empty(1, dtype=torch.int32, device=dev)
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    flush = torch.empty(a.flush_mib << 20, dtype=torch.uint8, device=dev) if a.flush_mib else None
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    P = lambda t: t.data_ptr()
+    c = W.WORKLOADS[a.workload]()
+    if a.workload == "expert_choice":
+        path = expert_choice_path(c, N, torch, dev, sp)
+    else:
+        path = token_choice_path(c, N, torch, dev, sp)
+    flush = torch.empty(a.flush_mib << 20, dtype=torch.uint8, device=dev) if a.flush_mib else None
+    if a.copy_probe_mib:
+        src = torch.ones(a.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1, out=dst)          # an elementwise kernel: reads and writes N MiB
+        torch.cuda.synchronize()
+        del src, dst
 
-    def layout():
-        N.ep_get_dispatch_layout(P(idx), T, K, E, 1, P(counts), P(offsets), P(tpr), P(itr),
-                                 P(ninv), P(ws), ws_bytes, sp)
-
-    def dispatch():
-        N.ep_dispatch(P(x), T, H, P(idx), K, E, P(offsets), N.EP_LAYOUT_CONTIGUOUS, rows,
-                      N.EP_QUANT_BF16, P(recv), None, P(slot), P(src), P(nd), P(ws), ws_bytes, sp)
-
-    def combine():
-        N.ep_combine(P(recv), rows, H, P(slot), P(w), T, K, P(out), sp)
+    def step():
+        for _, fn in path.ops:
+            fn()
 
     for _ in range(a.warmup):
-        layout(); dispatch(); combine()
+        step()
     torch.cuda.synchronize()
 
     # timed region: exactly K steps between two device synchronisations, with
@@ -145,49 +257,39 @@ def main():
     for i in range(a.steps):
         if flush is not None:
             flush.fill_(i & 0xFF)
-        layout(); dispatch(); combine()
+        step()
     r1.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / a.steps
     region_ms = r0.elapsed_time(r1) / a.steps
     ms_per_step = wall_ms if flush is None else region_ms
 
-    # per-operation kernel durations: a second pass of K steps with HIP
-    # events around each operation on the stream the kernels run on
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    # per-operation durations: a second pass of K steps with HIP events
+    # around each operation on the stream the kernels run on
+    nops = len(path.ops)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] for _ in range(a.steps)]
     for i in range(a.steps):
         if flush is not None:
             flush.fill_(i & 0xFF)
         e = ev[i]
-        e[0].record(stream); layout()
-        e[1].record(stream); dispatch()
-        e[2].record(stream); combine()
-        e[3].record(stream)
+        for j, (_, fn) in enumerate(path.ops):
+            e[j].record(stream)
+            fn()
+        e[nops].record(stream)
     torch.cuda.synchronize()
-    lay_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    dis_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    com_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    op_us = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]) * 1e3)
+             for j, (name, _) in enumerate(path.ops)}
+    step_ev = np.array([e[0].elapsed_time(e[nops]) for e in ev]) * 1e3
 
-    # algorithmic bytes (each x row read once, each received row written once
-    # and read once, each output row written once, plus index metadata)
-    row = H * 2
-    meta = 5 * T * K * 4
-    alg_total = T * row + N_valid * row + N_valid * row + T * row + meta
-    alg_dispatch = T * row + N_valid * row + 2 * T * K * 4
-    alg_combine = N_valid * row + T * row + 2 * T * K * 4
-    d_us, c_us = dis_ms.mean() * 1e3, com_ms.mean() * 1e3
-    if d_us >= c_us:
-        dom, dom_us, dom_bytes = "dispatch_kernel", d_us, alg_dispatch
-    else:
-        dom, dom_us, dom_bytes = "combine_kernel", c_us, alg_combine
+    alg_total = sum(path.alg_bytes.values())
+    dom = max(("dispatch", "combine"), key=lambda n: op_us[n])
+    dom_us, dom_bytes = op_us[dom], path.alg_bytes[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    traffic = traffic_entry(dom)
-
-    torch.cuda.synchronize()
+    headline = a.workload == "prefill"
     res = {
-        "metric": METRIC,
-        "value": T / (ms_per_step * 1e-3),
+        "metric": HEADLINE_METRIC if headline else
+                  f"dispatch+combine tokens/s & achieved HBM GB/s, {c.name}",
+        "value": path.T / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
@@ -196,24 +298,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3 dispatch, bf16 combine" if a.workload == "decode" else "bf16",
         "data": "synthetic",
-        "config": {"workload": c.name, "T": T, "H": H, "E": E, "top_k": K,
-                   "routing": "top-8 of N(0,1) logits + 2*log Zipf(1.2) expert bias",
-                   "recv_layout": "contiguous", "quant": "bf16", "combine": "weighted",
-                   "valid_slots": N_valid, "cold_flush_mib": a.flush_mib},
+        "config": {"workload": c.name, **path.meta, "cold_flush_mib": a.flush_mib},
         "achieved_GBps": alg_total / (ms_per_step * 1e-3) / 1e9,
         "frac_of_peak_hbm": alg_total / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "algorithmic_bytes_per_step": alg_total,
+        "algorithmic_bytes_per_op": path.alg_bytes,
         "timed_region_event_ms_per_step": region_ms,
-        "per_op_us": {"layout": float(lay_ms.mean() * 1e3), "dispatch": float(d_us),
-                      "combine": float(c_us), "step_with_op_events": float(step_ms.mean() * 1e3),
-                      "step_with_op_events_p10": float(np.percentile(step_ms, 10) * 1e3),
-                      "step_with_op_events_p90": float(np.percentile(step_ms, 90) * 1e3)},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": dom_bytes,
-                     "avg_launch_us": float(dom_us)},
+        "per_op_us": {**op_us, "step_with_op_events": float(step_ev.mean()),
+                      "step_with_op_events_p10": float(np.percentile(step_ev, 10)),
+                      "step_with_op_events_p90": float(np.percentile(step_ev, 90))},
+        "roofline": {"bound": "hbm", "kernel": path.kernel_of[dom], "op": dom,
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": traffic_entry(a.workload, path.kernel_of[dom]),
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": dom_us},
     }
     if a.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(c, a.cpu_budget)
