@@ -127,22 +127,25 @@ __device__ __forceinline__ uint64_t match_key(int key, bool active, int nbits)
     return active ? m : 0ull;
 }
 
-__device__ __forceinline__ int wave_sum(int v)
+// Inclusive prefix sum across the 64 lanes of a wave with DPP row shifts
+// (Hillis-Steele inside each 16-lane row), then row broadcasts of lane 15
+// into rows 1 and 3 and of lane 31 into rows 2 and 3.  Lanes whose DPP
+// source falls outside the row add 0.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int /*lane*/)
 {
-    for (int o = kWave / 2; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, kWave);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
     return v;
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
+// Sum over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ int wave_sum(int v)
 {
-    for (int o = 1; o < kWave; o <<= 1) {
-        int n = __shfl_up(v, o, kWave);
-        if (lane >= o)
-            v += n;
-    }
-    return v;
+    return __builtin_amdgcn_readlane(wave_inclusive_scan(v, 0), kWave - 1);
 }
 
 // Exclusive prefix sum over a block's threads (blockDim.x <= 1024, multiple

@@ -156,6 +156,7 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
             uint64_t m = 0;
             if (tl < ntok) {
                 const int32_t *row = ent + tl * K;
+#pragma unroll 8
                 for (int k = 0; k < K; ++k) {
                     const int ee = row[k];
                     if ((unsigned)ee < (unsigned)E)
@@ -196,8 +197,7 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
             }
         }
     }
-    inval = wave_sum(inval);
-    if (lane == 0 && inval)
+    if (inval)                                     // rare: no wave reduction
         atomicAdd(&tmp[31], inval);
     __syncthreads();
 
@@ -275,10 +275,17 @@ layout_scan_kernel(int nchunk, int E, int R, int32_t *__restrict__ chunk_hist,
             __syncthreads();
             if (tid < nc) {
                 int32_t *row = tile + tid * ld;
-                for (int c = 0; c < sl; ++c) {
-                    const int h = row[c];
-                    row[c] = carry;
-                    carry += h;
+                for (int c0 = 0; c0 < sl; c0 += 8) {    // 8 shared-memory reads in flight
+                    int h[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        h[u] = c0 + u < sl ? row[c0 + u] : 0;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (c0 + u < sl) {
+                            row[c0 + u] = carry;
+                            carry += h[u];
+                        }
                 }
             }
             __syncthreads();
