@@ -88,7 +88,10 @@ combine_kernel(const uint16_t *__restrict__ y, int y_rows, int H,
     store_row<PPT>(acc, out, H, t, seg0, pieces);
 }
 
-template <int PPT>
+// G entries per round: their row indices and weights are scalar loads, then
+// all G*PPT row pieces are requested before the first FMA, so a token that
+// many experts picked waits on ceil(m/G) memory round trips, not m.
+template <int PPT, int G>
 __global__ void __launch_bounds__(256)
 ec_combine_kernel(const uint16_t *__restrict__ y, const float *__restrict__ w, int n_ent, int H,
                   const int32_t *__restrict__ tok_off, const int32_t *__restrict__ tok_ent,
@@ -99,18 +102,45 @@ ec_combine_kernel(const uint16_t *__restrict__ y, const float *__restrict__ w, i
     const int seg0 = blockIdx.y * PPT * blockDim.x;
     float acc[PPT][8];
 #pragma unroll
-    for (int j = 0; j < PPT; ++j)
+    for (int k = 0; k < PPT; ++k)
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-            acc[j][u] = 0.0f;
+            acc[k][u] = 0.0f;
     const int b = tok_off[t], e = tok_off[t + 1];
     const int n = (b >= 0 && e >= b && e <= n_ent) ? e - b : 0;
-    for (int a = 0; a < n; ++a) {
-        const int j = tok_ent[b + a];
-        if ((unsigned)j >= (unsigned)n_ent)
-            continue;
-        acc_row<PPT>(acc, reinterpret_cast<const char *>(y) + (size_t)j * H * 2, w[j], seg0,
-                     pieces);
+    for (int a0 = 0; a0 < n; a0 += G) {
+        bool ok[G];
+        float wk[G];
+        u32x4 v[G][PPT];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int j = a0 + g < n ? tok_ent[b + a0 + g] : -1;
+            ok[g] = (unsigned)j < (unsigned)n_ent;
+            const size_t row = ok[g] ? (size_t)j : 0;
+            wk[g] = ok[g] ? w[row] : 0.0f;
+            // an entry that is not used gets a zero-length descriptor: no access
+            const rsrc_t src = row_rsrc(reinterpret_cast<const char *>(y) + row * H * 2,
+                                        ok[g] ? pieces * 16 : 0);
+#pragma unroll
+            for (int k = 0; k < PPT; ++k)
+                v[g][k] = row_ld16(src, (seg0 + threadIdx.x + k * blockDim.x) * 16);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (!ok[g])
+                continue;
+#pragma unroll
+            for (int k = 0; k < PPT; ++k) {
+                acc[k][0] = fmaf(wk[g], bf16_lo(v[g][k].x), acc[k][0]);
+                acc[k][1] = fmaf(wk[g], bf16_hi(v[g][k].x), acc[k][1]);
+                acc[k][2] = fmaf(wk[g], bf16_lo(v[g][k].y), acc[k][2]);
+                acc[k][3] = fmaf(wk[g], bf16_hi(v[g][k].y), acc[k][3]);
+                acc[k][4] = fmaf(wk[g], bf16_lo(v[g][k].z), acc[k][4]);
+                acc[k][5] = fmaf(wk[g], bf16_hi(v[g][k].z), acc[k][5]);
+                acc[k][6] = fmaf(wk[g], bf16_lo(v[g][k].w), acc[k][6]);
+                acc[k][7] = fmaf(wk[g], bf16_hi(v[g][k].w), acc[k][7]);
+            }
+        }
     }
     store_row<PPT>(acc, out, H, t, seg0, pieces);
 }
@@ -182,18 +212,16 @@ hipError_t launch_ec_combine(const uint16_t *y, const float *w, int E, int C, in
 {
     if (T == 0)
         return hipSuccess;
-    // Tokens picked by many experts read many rows: spread each row over
-    // more blocks (fewer pieces per thread) so a popular token's work is
-    // shared by several CUs.
+    // At most 2 pieces per thread (so a popular token's row is spread over
+    // more blocks) and 16 row pieces in flight per thread.
     RowShape rs = row_shape(H / 8, 2);
     dim3 grid(T, rs.nseg), block(rs.bd);
-#define EP_EC_COMBINE_CASE(N)                                                                    \
-    case N:                                                                                      \
-        hipLaunchKernelGGL((ec_combine_kernel<N>), grid, block, 0, s, y, w, E * C, H, tok_off,    \
-                           tok_ent, out);                                                        \
-        break;
-    EP_PPT_SWITCH(rs.ppt, EP_EC_COMBINE_CASE)
-#undef EP_EC_COMBINE_CASE
+    if (rs.ppt == 1)
+        hipLaunchKernelGGL((ec_combine_kernel<1, 16>), grid, block, 0, s, y, w, E * C, H, tok_off,
+                           tok_ent, out);
+    else
+        hipLaunchKernelGGL((ec_combine_kernel<2, 8>), grid, block, 0, s, y, w, E * C, H, tok_off,
+                           tok_ent, out);
     return hipGetLastError();
 }
 

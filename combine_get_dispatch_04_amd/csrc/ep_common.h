@@ -58,6 +58,11 @@ __device__ __forceinline__ u32x4 row_ld16(rsrc_t r, int off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy);
 }
+// Default policy, for rows that other blocks read again.
+__device__ __forceinline__ u32x4 row_ld16_cached(rsrc_t r, int off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
 
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

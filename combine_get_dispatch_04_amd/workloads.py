@@ -194,14 +194,29 @@ def random_token_choice(seed: int, T: int, H: int, E: int, K: int, p_pad: float 
 
 
 def random_expert_choice(seed: int, T: int, H: int, E: int, C: int, p_empty: float = 0.1,
-                         p_invalid: float = 0.0, hot: int = 0) -> ExpertChoice:
+                         p_invalid: float = 0.0, hot: int = 0,
+                         distinct: bool = False) -> ExpertChoice:
     """Uniform token picks (duplicates allowed, as with randint), optional
-    -1 entries, invalid values, and `hot` tokens that every expert picks."""
+    -1 entries, invalid values, and `hot` tokens that every expert picks.
+    With `distinct` (needs C <= T) no expert picks a token twice, as in
+    top-C selection: each row is a random sample without replacement, and
+    the hot tokens are distinct too."""
     rng = np.random.default_rng(seed)
     x = bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
-    ti = rng.integers(0, max(T, 1), size=(E, C), dtype=np.int64)
-    if hot > 0 and T > 0:
-        ti[:, :min(hot, C)] = rng.integers(0, T, size=min(hot, C))[None, :]
+    if distinct:
+        assert C <= T
+        h = min(hot, C)
+        hot_set = rng.choice(T, size=h, replace=False)
+        rest = np.setdiff1d(np.arange(T), hot_set)
+        ti = np.empty((E, C), np.int64)
+        for e in range(E):
+            ti[e, :h] = hot_set
+            ti[e, h:] = rng.choice(rest, size=C - h, replace=False)
+            rng.shuffle(ti[e])
+    else:
+        ti = rng.integers(0, max(T, 1), size=(E, C), dtype=np.int64)
+        if hot > 0 and T > 0:
+            ti[:, :min(hot, C)] = rng.integers(0, T, size=min(hot, C))[None, :]
     u = rng.random((E, C))
     ti = np.where(u < p_empty, -1, ti)
     bad = (u >= p_empty) & (u < p_empty + p_invalid)

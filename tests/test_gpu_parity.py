@@ -261,21 +261,41 @@ def test_combine_unit_weights_round_trip_exact():
 
 
 # ---------------------------------------------------------------- expert choice
+# The inverse map is built by one block from per-token expert bitmasks in
+# LDS, or, when some expert lists a token twice, by the same block with
+# counters and a rank sort.  That block runs inside the copy's launch when
+# the T*ceil(E/64) mask words take at most 81664 bytes, in a launch of its
+# own up to the device's LDS per block (160 KiB), and beyond that five
+# launches do the work with the counters in the workspace.
 EC_CASES = [
-    # T, H, E, C, p_empty, p_invalid, hot
-    (1, 8, 1, 1, 0.0, 0.0, 0),
-    (10, 24, 3, 4, 0.2, 0.1, 0),
-    (500, 520, 16, 64, 0.1, 0.02, 5),
-    (300, 4096, 64, 40, 0.0, 0.0, 40),          # tokens picked by all 64 experts
-    (50, 64, 1200, 2, 0.0, 0.0, 1),              # one token picked 1200 times (> one sort tile)
-    (0, 16, 3, 5, 0.0, 0.0, 0),                  # no tokens: every entry is -1
+    # T, H, E, C, p_empty, p_invalid, hot, distinct
+    (1, 8, 1, 1, 0.0, 0.0, 0, False),
+    (10, 24, 3, 4, 0.2, 0.1, 0, False),
+    (500, 520, 16, 64, 0.1, 0.02, 5, False),
+    (300, 4096, 64, 40, 0.0, 0.0, 40, False),    # tokens picked by all 64 experts
+    (50, 64, 1200, 2, 0.0, 0.0, 1, False),       # one token picked 1200 times (> one sort tile)
+    (0, 16, 3, 5, 0.0, 0.0, 0, False),           # no tokens: every entry is -1
+    (0, 16, 3, 5, 0.0, 0.3, 0, False),           # no tokens, some entries invalid
+    (500, 520, 16, 64, 0.1, 0.05, 5, True),      # bitmask path, empty and invalid entries
+    (64, 40, 64, 64, 0.0, 0.0, 64, True),        # every expert picks every token (bit 63 used)
+    (300, 96, 100, 20, 0.05, 0.0, 7, True),      # two mask words per token
+    (64, 8, 130, 8, 0.0, 0.0, 3, True),          # three mask words, hot tokens in all of them
+    (1, 8, 5, 1, 0.0, 0.0, 1, True),             # one token, every expert
+    (5000, 8, 32, 200, 0.0, 0.0, 0, False),      # duplicate path at a larger T
+    (10200, 8, 8, 1000, 0.1, 0.01, 3, True),     # 81600 B of masks: inside the copy's launch
+    (13000, 8, 8, 1000, 0.1, 0.01, 3, True),     # 104000 B: a launch of its own
+    (20000, 8, 8, 1000, 0.1, 0.01, 3, True),     # 160000 B: a launch of its own
+    (20000, 8, 8, 1000, 0.0, 0.0, 0, False),     # 160000 B with duplicates
+    (30000, 8, 8, 512, 0.1, 0.01, 3, True),      # 240000 B: five launches
+    (30000, 16, 4, 600, 0.0, 0.0, 2, False),     # five launches with duplicates
 ]
 
 
-@pytest.mark.parametrize("T,H,E,C,pe,pi,hot", EC_CASES)
-def test_expert_choice_parity(T, H, E, C, pe, pi, hot):
-    _announce(f"ec T={T} H={H} E={E} C={C} hot={hot}")
-    c = W.random_expert_choice(T + E * C, T, H, E, C, p_empty=pe, p_invalid=pi, hot=hot)
+@pytest.mark.parametrize("T,H,E,C,pe,pi,hot,distinct", EC_CASES)
+def test_expert_choice_parity(T, H, E, C, pe, pi, hot, distinct):
+    _announce(f"ec T={T} H={H} E={E} C={C} hot={hot} distinct={distinct}")
+    c = W.random_expert_choice(T + E * C, T, H, E, C, p_empty=pe, p_invalid=pi, hot=hot,
+                               distinct=distinct)
     x_d, ti_d = G.dev(c.x), G.dev(c.token_indices)
     recv, off, ent, ninv = G.ec_dispatch(x_d, ti_d)
     torch.cuda.synchronize()
