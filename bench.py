@@ -15,7 +15,9 @@ outside the timed region), expert_choice (ep_dispatch_expert_choice +
 ep_combine_expert_choice), large_padded.
 
 Also reported: per-operation times (HIP events on the stream the kernels run
-on, in a second pass after the timed region), the roofline of the dominant
+on, in a second pass after the timed region), a cold-cache pass (1 GiB of
+scratch written before each step, outside its events, so that neither L2 nor
+the 256 MB MALL holds the inputs), the roofline of the dominant
 kernel (algorithmic bytes per launch over its average duration, against
 8 TB/s), HBM traffic from the committed rocprofv3 counter summary when it was
 taken on the current kernel sources, and the CPU oracle timed on the host on
@@ -158,7 +160,7 @@ def expert_choice_path(c, N, torch, dev, sp):
 
     alg = {"dispatch": U * H * 2 + n_valid * H * 2 + E * C * 4 + (T + 1) * 4 + n_valid * 4,
            "combine": n_valid * H * 2 + T * H * 2 + E * C * 4 + (T + 1) * 4 + n_valid * 4}
-    kern = {"dispatch": "ec_sort_copy_kernel", "combine": "ec_combine_kernel"}
+    kern = {"dispatch": "ec_dispatch_fused_kernel", "combine": "ec_combine_kernel"}
     meta = {"T": T, "H": H, "E": E, "capacity": C, "valid_entries": n_valid,
             "distinct_tokens": U}
     return Path(c.name, T, [("dispatch", dispatch), ("combine", combine)], kern, alg, meta)
@@ -207,8 +209,9 @@ def main():
                     choices=["prefill", "toy", "decode", "expert_choice", "large_padded"])
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
-    ap.add_argument("--flush-mib", type=int, default=0,
-                    help="write this many MiB of scratch before each step (cold caches)")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="cold pass: write this many MiB of scratch before each step, "
+                         "outside the step's events (0 = no cold pass)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     a = ap.parse_args()
@@ -255,22 +258,17 @@ def main():
     t0 = time.perf_counter()
     r0.record(stream)
     for i in range(a.steps):
-        if flush is not None:
-            flush.fill_(i & 0xFF)
         step()
     r1.record(stream)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / a.steps
     region_ms = r0.elapsed_time(r1) / a.steps
-    ms_per_step = wall_ms if flush is None else region_ms
 
     # per-operation durations: a second pass of K steps with HIP events
     # around each operation on the stream the kernels run on
     nops = len(path.ops)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] for _ in range(a.steps)]
     for i in range(a.steps):
-        if flush is not None:
-            flush.fill_(i & 0xFF)
         e = ev[i]
         for j, (_, fn) in enumerate(path.ops):
             e[j].record(stream)
@@ -280,6 +278,26 @@ def main():
     op_us = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]) * 1e3)
              for j, (name, _) in enumerate(path.ops)}
     step_ev = np.array([e[0].elapsed_time(e[nops]) for e in ev]) * 1e3
+
+    # cold pass: before each step (outside its events) write flush_mib MiB of
+    # scratch, which evicts L2 and the 256 MB MALL
+    cold = None
+    if flush is not None:
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(a.steps)]
+        for i in range(a.steps):
+            flush.fill_(i & 0xFF)
+            cev[i][0].record(stream)
+            step()
+            cev[i][1].record(stream)
+        torch.cuda.synchronize()
+        cus = np.array([b_.elapsed_time(e_) for b_, e_ in cev]) * 1e3
+        med = float(np.median(cus))
+        cold = {"flush_mib": a.flush_mib, "us_per_step_median": med,
+                "us_per_step_p10": float(np.percentile(cus, 10)),
+                "us_per_step_p90": float(np.percentile(cus, 90)),
+                "tokens_per_s": path.T / (med * 1e-6),
+                "achieved_GBps": sum(path.alg_bytes.values()) / (med * 1e-6) / 1e9}
 
     alg_total = sum(path.alg_bytes.values())
     dom = max(("dispatch", "combine"), key=lambda n: op_us[n])
@@ -300,7 +318,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8_e4m3 dispatch, bf16 combine" if a.workload == "decode" else "bf16",
         "data": "synthetic",
-        "config": {"workload": c.name, **path.meta, "cold_flush_mib": a.flush_mib},
+        "config": {"workload": c.name, **path.meta},
         "achieved_GBps": alg_total / (ms_per_step * 1e-3) / 1e9,
         "frac_of_peak_hbm": alg_total / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "algorithmic_bytes_per_step": alg_total,
@@ -315,6 +333,7 @@ def main():
                      "traffic": traffic_entry(a.workload, path.kernel_of[dom]),
                      "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": dom_us},
     }
+    res["cold"] = cold
     if a.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(c, a.cpu_budget)
     print(json.dumps(res), flush=True)
