@@ -50,6 +50,16 @@ def lib():
         L.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_to_f32.restype = ctypes.c_float
         L.oracle_e4m3_from_f32_array.argtypes = [_P, _P, _I64]
+        L.oracle_e5m2_from_f32_array.argtypes = [_P, _P, _I64]
+        L.oracle_e2m1_from_f32_array.argtypes = [_P, _P, _I64]
+        L.oracle_e5m2_to_f32.argtypes = [ctypes.c_uint8]
+        L.oracle_e5m2_to_f32.restype = ctypes.c_float
+        L.oracle_e2m1_to_f32.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_to_f32.restype = ctypes.c_float
+        L.oracle_int8_from_f32.argtypes = [ctypes.c_float]
+        L.oracle_int8_from_f32.restype = ctypes.c_int8
+        L.oracle_dispatch_token_quant.argtypes = [_P, _I, _I, _P, _I, _I, _P, _P]
+        L.oracle_dispatch_mx.argtypes = [_P, _I, _I, _P, _I, _I, _P, _P]
         L.oracle_bf16_from_f64_array.argtypes = [_P, _P, _I64]
         L.oracle_layout.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P]
         L.oracle_slots.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _P]
@@ -61,7 +71,9 @@ def lib():
         L.oracle_ec_combine.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P]
         for f in ("oracle_layout", "oracle_slots", "oracle_dispatch_bf16", "oracle_dispatch_fp8",
                   "oracle_combine", "oracle_ec_dispatch", "oracle_ec_invert", "oracle_ec_combine",
-                  "oracle_e4m3_from_f32_array", "oracle_bf16_from_f64_array"):
+                  "oracle_e4m3_from_f32_array", "oracle_bf16_from_f64_array",
+                  "oracle_e5m2_from_f32_array", "oracle_e2m1_from_f32_array",
+                  "oracle_dispatch_token_quant", "oracle_dispatch_mx"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -86,6 +98,32 @@ def e4m3_from_f32(v: np.ndarray) -> np.ndarray:
 
 def e4m3_to_f32(code: int) -> float:
     return lib().oracle_e4m3_to_f32(int(code))
+
+
+def e5m2_from_f32(v: np.ndarray) -> np.ndarray:
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().oracle_e5m2_from_f32_array(_p(v), _p(out), v.size)
+    return out
+
+
+def e5m2_to_f32(code: int) -> float:
+    return lib().oracle_e5m2_to_f32(int(code))
+
+
+def e2m1_from_f32(v: np.ndarray) -> np.ndarray:
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().oracle_e2m1_from_f32_array(_p(v), _p(out), v.size)
+    return out
+
+
+def e2m1_to_f32(code: int) -> float:
+    return lib().oracle_e2m1_to_f32(int(code))
+
+
+def int8_from_f32(v: float) -> int:
+    return int(lib().oracle_int8_from_f32(float(v)))
 
 
 def bf16_from_f64(v: np.ndarray) -> np.ndarray:
@@ -144,6 +182,37 @@ def dispatch_fp8(x: np.ndarray, slot: np.ndarray, rows: int):
     s = np.zeros((rows, H // 128), np.float32)
     lib().oracle_dispatch_fp8(_p(x), T, H, _p(slot), K, _p(q), _p(s))
     return q, s
+
+
+TOKEN_FMT = {"fp8_e4m3_token": 0, "int8_token": 1}
+MX_FMT = {"mxfp8_e4m3": 0, "mxfp8_e5m2": 1, "mxfp4_e2m1": 2}
+
+
+def dispatch_token_quant(x: np.ndarray, slot: np.ndarray, rows: int, mode: str):
+    """Per-token scaled quantisation ("fp8_e4m3_token" or "int8_token"):
+    -> (codes [rows, H] uint8, scales [rows] float32)."""
+    x = _c(x, np.uint16)
+    slot = _c(slot, np.int32)
+    T, H = x.shape
+    K = slot.shape[1]
+    q = np.zeros((rows, H), np.uint8)
+    s = np.zeros(rows, np.float32)
+    lib().oracle_dispatch_token_quant(_p(x), T, H, _p(slot), K, TOKEN_FMT[mode], _p(q), _p(s))
+    return q, s
+
+
+def dispatch_mx(x: np.ndarray, slot: np.ndarray, rows: int, mode: str):
+    """MX quantisation ("mxfp8_e4m3", "mxfp8_e5m2", "mxfp4_e2m1"):
+    -> (codes [rows, H or H/2] uint8, e8m0 scale codes [rows, H/32] uint8)."""
+    x = _c(x, np.uint16)
+    slot = _c(slot, np.int32)
+    T, H = x.shape
+    K = slot.shape[1]
+    fmt = MX_FMT[mode]
+    q = np.zeros((rows, H // 2 if fmt == 2 else H), np.uint8)
+    e = np.zeros((rows, H // 32), np.uint8)
+    lib().oracle_dispatch_mx(_p(x), T, H, _p(slot), K, fmt, _p(q), _p(e))
+    return q, e
 
 
 def combine(y: np.ndarray, slot: np.ndarray, w=None):

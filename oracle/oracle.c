@@ -298,6 +298,215 @@ void oracle_dispatch_fp8(const uint16_t *x, int T, int H, const int32_t *slot, i
     free(s);
 }
 
+/* ------------------------------------------------------------------ */
+/* The other quantisation modes of [EPA] "Quantization Modes in Normal    */
+/* Dispatch": INT8 dynamic (int8, float32 scale, per token), scalar FP8   */
+/* (float8_e4m3fn, float32 scale, per token), MXFP8 per-block             */
+/* (float8_e4m3fn or float8_e5m2 with a float8_e8m0fnu scale per 32       */
+/* elements) and MXFP4 (float4_e2m1fn_x2 with the same scales).  The      */
+/* table fixes formats and granularities only; the rules taken are stated */
+/* at each function.                                                      */
+/* ------------------------------------------------------------------ */
+
+/* Round a >= 0 (fp64, exact) to the nearest value of a binary format with
+ * `mbits` fraction bits and smallest normal exponent `emin` (so the
+ * subnormal quantum is 2^(emin - mbits)), ties to the even significand;
+ * results above `maxv` saturate to `maxv`. */
+static double round_to_format(double a, int mbits, int emin, double maxv)
+{
+    if (a == 0.0)
+        return 0.0;
+    int e;
+    frexp(a, &e);
+    int ex = e - 1;                                   /* floor(log2(a)) */
+    int qexp = (ex < emin) ? emin - mbits : ex - mbits;
+    double r = ldexp(nearbyint(ldexp(a, -qexp)), qexp);
+    return r > maxv ? maxv : r;
+}
+
+/* The code (without sign) of a value r of that format, exponent bias `bias`. */
+static unsigned code_of(double r, int mbits, int emin, int bias)
+{
+    if (r == 0.0)
+        return 0u;
+    int e;
+    frexp(r, &e);
+    int ex = e - 1;
+    if (ex < emin)                                    /* subnormal: r = m * 2^(emin - mbits) */
+        return (unsigned)ldexp(r, mbits - emin);
+    unsigned m = (unsigned)ldexp(r, mbits - ex) - (1u << mbits);
+    return ((unsigned)(ex + bias) << mbits) | m;
+}
+
+/* OCP 8-bit E5M2 ("float8_e5m2"): bias 15, 2 fraction bits, largest finite
+ * 1.75 * 2^15 = 57344, subnormals m * 2^-16.  Round to nearest even; the
+ * format has infinities, but magnitudes beyond 57344 saturate to it
+ * (reading: a quantised payload stays finite, as with E4M3).  Sign of zero
+ * kept. */
+uint8_t oracle_e5m2_from_f32(float v)
+{
+    unsigned sign = signbit(v) ? 0x80u : 0u;
+    double r = round_to_format(fabs((double)v), 2, -14, 57344.0);
+    return (uint8_t)(sign | code_of(r, 2, -14, 15));
+}
+
+float oracle_e5m2_to_f32(uint8_t c)
+{
+    int s = (c >> 7) & 1, ef = (c >> 2) & 31, m = c & 3;
+    double v;
+    if (ef == 31)
+        return m ? NAN : (s ? -INFINITY : INFINITY);
+    v = ef == 0 ? ldexp((double)m, -16) : ldexp(4.0 + m, ef - 15 - 2);
+    return (float)(s ? -v : v);
+}
+
+/* OCP 4-bit E2M1 ("float4_e2m1fn"): bias 1, 1 fraction bit; the magnitudes
+ * are 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7), bit 3 is the sign.  Round to
+ * nearest even; beyond 6 saturates to 6.  Sign of zero kept. */
+uint8_t oracle_e2m1_from_f32(float v)
+{
+    unsigned sign = signbit(v) ? 0x8u : 0u;
+    double r = round_to_format(fabs((double)v), 1, 0, 6.0);
+    return (uint8_t)(sign | code_of(r, 1, 0, 1));
+}
+
+float oracle_e2m1_to_f32(uint8_t c)
+{
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double v = mag[c & 7];
+    return (float)((c & 8) ? -v : v);
+}
+
+/* int8 code of v: round to nearest, ties to even, clamped to [-127, 127]
+ * (reading: the symmetric range, so that -q is always a code). */
+int8_t oracle_int8_from_f32(float v)
+{
+    double q = nearbyint((double)v);
+    if (q > 127.0)
+        q = 127.0;
+    if (q < -127.0)
+        q = -127.0;
+    return (int8_t)q;
+}
+
+void oracle_e5m2_from_f32_array(const float *in, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e5m2_from_f32(in[i]);
+}
+
+void oracle_e2m1_from_f32_array(const float *in, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e2m1_from_f32(in[i]);
+}
+
+/* Per-token scaled dispatch: INT8 dynamic (fmt 1) and scalar FP8 (fmt 0).
+ * Rule taken (the same shape as the 128-channel fp8 rule, over the whole
+ * row): per token t
+ *   a = max over the row of |x|                         (exact)
+ *   a == 0: s = 0 and every code is 0
+ *   else:   s = a / Q  (fp32 division, RNE), Q = 448 (e4m3) or 127 (int8)
+ *           q_i = enc(x_i / s)  (fp32 division, then the RNE encoder)
+ * recv_q [rows, H] codes (int8 as two's complement bytes), recv_s [rows]. */
+void oracle_dispatch_token_quant(const uint16_t *x, int T, int H, const int32_t *slot, int K,
+                                 int fmt, uint8_t *recv_q, float *recv_s)
+{
+    uint8_t *q = (uint8_t *)malloc((size_t)H + 1);
+    const float Q = fmt == 1 ? 127.0f : 448.0f;
+    for (int t = 0; t < T; ++t) {
+        const uint16_t *xr = x + (int64_t)t * H;
+        float a = 0.0f;
+        for (int i = 0; i < H; ++i) {
+            float v = fabsf(oracle_bf16_to_f32(xr[i]));
+            if (v > a)
+                a = v;
+        }
+        float st = 0.0f;
+        if (a == 0.0f) {
+            memset(q, 0, (size_t)H);
+        } else {
+            st = a / Q;
+            for (int i = 0; i < H; ++i) {
+                float v = oracle_bf16_to_f32(xr[i]) / st;
+                q[i] = fmt == 1 ? (uint8_t)oracle_int8_from_f32(v) : oracle_e4m3_from_f32(v);
+            }
+        }
+        for (int k = 0; k < K; ++k) {
+            int32_t sl = slot[(int64_t)t * K + k];
+            if (sl < 0)
+                continue;
+            memcpy(recv_q + (int64_t)sl * H, q, (size_t)H);
+            recv_s[sl] = st;
+        }
+    }
+    free(q);
+}
+
+/* MX dispatch (MXFP8 e4m3: fmt 0, MXFP8 e5m2: fmt 1, MXFP4 e2m1: fmt 2).
+ * Rule taken (the shared-scale rule of the OCP microscaling formats): per
+ * token and block b of 32 consecutive channels
+ *   a = max |x| over the block
+ *   E = floor(log2(a)) - emax, emax = 8 (e4m3), 15 (e5m2), 2 (e2m1),
+ *       clamped to [-127, 127]; an all-zero block takes E = -127
+ *   scale code = E + 127 (float8_e8m0fnu: the value 2^E)
+ *   element i = enc(x_i * 2^-E)  (exact power-of-two scaling, then the RNE
+ *               encoder, saturating)
+ * recv_q rows are H bytes (fp8) or H/2 bytes (fp4: channel 2i in the low
+ * nibble of byte i, channel 2i+1 in the high nibble); recv_e [rows, H/32]. */
+void oracle_dispatch_mx(const uint16_t *x, int T, int H, const int32_t *slot, int K, int fmt,
+                        uint8_t *recv_q, uint8_t *recv_e)
+{
+    static const int emax_of[3] = {8, 15, 2};
+    const int emax = emax_of[fmt];
+    const int nb = H / 32;
+    const int rb = fmt == 2 ? H / 2 : H;
+    uint8_t *q = (uint8_t *)malloc((size_t)rb + 1);
+    uint8_t *ec = (uint8_t *)malloc((size_t)nb + 1);
+    for (int t = 0; t < T; ++t) {
+        const uint16_t *xr = x + (int64_t)t * H;
+        memset(q, 0, (size_t)rb);
+        for (int b = 0; b < nb; ++b) {
+            double a = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                double v = fabs((double)oracle_bf16_to_f32(xr[32 * b + i]));
+                if (v > a)
+                    a = v;
+            }
+            int E = -127;
+            if (a > 0.0) {
+                int e;
+                frexp(a, &e);
+                E = (e - 1) - emax;
+                if (E < -127)
+                    E = -127;
+                if (E > 127)
+                    E = 127;
+            }
+            ec[b] = (uint8_t)(E + 127);
+            for (int i = 0; i < 32; ++i) {
+                const int c = 32 * b + i;
+                float v = (float)ldexp((double)oracle_bf16_to_f32(xr[c]), -E);
+                if (fmt == 0)
+                    q[c] = oracle_e4m3_from_f32(v);
+                else if (fmt == 1)
+                    q[c] = oracle_e5m2_from_f32(v);
+                else
+                    q[c >> 1] |= (uint8_t)(oracle_e2m1_from_f32(v) << (4 * (c & 1)));
+            }
+        }
+        for (int k = 0; k < K; ++k) {
+            int32_t sl = slot[(int64_t)t * K + k];
+            if (sl < 0)
+                continue;
+            memcpy(recv_q + (int64_t)sl * rb, q, (size_t)rb);
+            memcpy(recv_e + (int64_t)sl * nb, ec, (size_t)nb);
+        }
+    }
+    free(q);
+    free(ec);
+}
+
 /* Combine ([EPA] API Overview: combine reduces the dispatched rows through
  * the handle; low_latency_combine also takes topk_weights):
  *   out[t, h] = bf16( sum over k with slot >= 0 of w[t,k] * y[slot[t,k], h] )

@@ -174,3 +174,76 @@ def multiplicity_times_x(x_bits, m):
     prod = (xf * np.asarray(m, np.float32)[:, None]).astype(np.float32)
     prod = np.where(prod == 0, np.float32(0.0), prod)
     return torch.from_numpy(np.ascontiguousarray(prod)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _nearest_code(v, codes, vals, maxv, sign_bit):
+    """Nearest code to each value among (codes, vals) of non-negative
+    magnitudes, ties to the even code, magnitudes above maxv saturating."""
+    v = np.asarray(v, np.float64)
+    a = np.minimum(np.abs(v), 2.0 * maxv)
+    d = np.abs(a[:, None] - vals[None, :])
+    cand = d == d.min(axis=1, keepdims=True)
+    even = (codes % 2 == 0)[None, :]
+    pick_even = cand & even
+    choose = np.where(pick_even.any(axis=1)[:, None], pick_even, cand)
+    code = codes[np.argmax(choose, axis=1)]
+    return (code | np.where(np.signbit(v), sign_bit, 0)).astype(np.uint8)
+
+
+def e5m2_table():
+    """Value of every non-negative finite E5M2 code 0x00..0x7B, listed from
+    the bit fields: exponent field f (bias 15), 2 fraction bits."""
+    codes = np.arange(0x7C)
+    vals = np.array([(c & 3) * 2.0 ** -16 if (c >> 2) == 0 else (1 + (c & 3) / 4) * 2.0 ** ((c >> 2) - 15)
+                     for c in codes])
+    return codes, vals
+
+
+def e5m2_nearest(v):
+    codes, vals = e5m2_table()
+    return _nearest_code(v, codes, vals, 57344.0, 0x80)
+
+
+def e2m1_nearest(v):
+    codes = np.arange(8)
+    vals = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    return _nearest_code(v, codes, vals, 6.0, 0x8)
+
+
+def int8_token_quant(xrow_bits):
+    """Per-token int8: numpy float32 division and np.rint (half to even)."""
+    x = bf16_to_f64(xrow_bits).astype(np.float32)
+    a = np.float32(np.abs(x).max())
+    if a == 0:
+        return np.zeros(x.size, np.uint8), np.float32(0)
+    s = np.float32(a / np.float32(127.0))
+    q = np.clip(np.rint((x / s).astype(np.float32)), -127, 127).astype(np.int8)
+    return q.view(np.uint8), s
+
+
+def mx_quant_row(xrow_bits, fmt):
+    """MX quantisation of one row with numpy: block exponent from np.frexp,
+    exact scaling by np.ldexp, elements by brute-force nearest-code search."""
+    emax = {"mxfp8_e4m3": 8, "mxfp8_e5m2": 15, "mxfp4_e2m1": 2}[fmt]
+    near = {"mxfp8_e4m3": e4m3_nearest, "mxfp8_e5m2": e5m2_nearest, "mxfp4_e2m1": e2m1_nearest}[fmt]
+    x = bf16_to_f64(xrow_bits)
+    H = x.size
+    codes = np.zeros(H, np.uint8)
+    ecode = np.zeros(H // 32, np.uint8)
+    for b in range(H // 32):
+        blk = x[32 * b:32 * (b + 1)]
+        a = np.abs(blk).max()
+        E = -127
+        if a > 0:
+            E = int(np.clip(np.frexp(a)[1] - 1 - emax, -127, 127))
+        ecode[b] = E + 127
+        scaled = np.ldexp(blk, -E)
+        if fmt == "mxfp8_e4m3":
+            # e4m3_nearest takes fp32; scaled values below fp32's range only
+            # occur far below the smallest subnormal code, where they give 0
+            codes[32 * b:32 * (b + 1)] = near(scaled.astype(np.float32))
+        else:
+            codes[32 * b:32 * (b + 1)] = near(scaled)
+    if fmt == "mxfp4_e2m1":
+        codes = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    return codes, ecode
