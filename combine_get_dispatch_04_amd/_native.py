@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(_PKG, "libep.so")
 
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_WORKSPACE, EP_ERR_HIP = range(5)
 EP_LAYOUT_CONTIGUOUS, EP_LAYOUT_PADDED = 0, 1
-EP_QUANT_BF16, EP_QUANT_FP8_E4M3_G128 = 0, 1
+(EP_QUANT_BF16, EP_QUANT_FP8_E4M3_G128, EP_QUANT_FP8_E4M3_TOKEN, EP_QUANT_INT8_TOKEN,
+ EP_QUANT_MXFP8_E4M3, EP_QUANT_MXFP8_E5M2, EP_QUANT_MXFP4_E2M1) = range(7)
 
 # name -> (restype, argtypes); every pointer is passed as an integer address
 _P = ctypes.c_void_p

@@ -96,6 +96,24 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int
     return Layout(tpr, None, counts, itr, offsets, ninv, topk_idx, E, R, ws)
 
 
+# quant name -> (ep_quant_t, receive dtype, H divisor of a receive row,
+# scale shape: H -> (columns or 0 for one per row, dtype), or None)
+_QUANT = {
+    "bf16": (N.EP_QUANT_BF16, torch.bfloat16, 1, None),
+    "fp8_e4m3_g128": (N.EP_QUANT_FP8_E4M3_G128, torch.float8_e4m3fn, 1,
+                      lambda H: (H // 128, torch.float32)),
+    "fp8_e4m3_token": (N.EP_QUANT_FP8_E4M3_TOKEN, torch.float8_e4m3fn, 1,
+                       lambda H: (0, torch.float32)),
+    "int8_token": (N.EP_QUANT_INT8_TOKEN, torch.int8, 1, lambda H: (0, torch.float32)),
+    "mxfp8_e4m3": (N.EP_QUANT_MXFP8_E4M3, torch.float8_e4m3fn, 1, lambda H: (H // 32, torch.uint8)),
+    "mxfp8_e5m2": (N.EP_QUANT_MXFP8_E5M2, torch.float8_e5m2, 1, lambda H: (H // 32, torch.uint8)),
+    "mxfp4_e2m1": (N.EP_QUANT_MXFP4_E2M1, torch.uint8, 2, lambda H: (H // 32, torch.uint8)),
+}
+_QUANT_ALIASES = {"pertoken_fp8_e4m3": "fp8_e4m3_token", "int8": "int8_token",
+                  "mx_fp8_e4m3": "mxfp8_e4m3", "mx_fp8_e5m2": "mxfp8_e5m2",
+                  "mx_fp4_e2m1": "mxfp4_e2m1"}
+
+
 def dispatch(x: torch.Tensor, layout: Layout, *, quant: str = "bf16",
              recv_layout: str = "contiguous", cap: Optional[int] = None,
              max_rows: Optional[int] = None):
@@ -103,20 +121,26 @@ def dispatch(x: torch.Tensor, layout: Layout, *, quant: str = "bf16",
 
     recv_layout "contiguous": expert blocks back to back, `max_rows` rows
     (default T*K, always enough).  "padded": [E, cap] rows, the low-latency
-    form.  quant "bf16" or "fp8_e4m3_g128" (e4m3 codes + fp32 scale per 128
-    channels)."""
+    form.  quant (names of the DeepEP-Ascend quantisation modes in
+    parentheses):
+      "bf16"                                 recv bf16 [rows, H], no scales
+      "fp8_e4m3_g128"                        e4m3 [rows, H] + fp32 [rows, H/128]
+      "fp8_e4m3_token" ("pertoken_fp8_e4m3") e4m3 [rows, H] + fp32 [rows]
+      "int8_token" ("int8")                  int8 [rows, H] + fp32 [rows]
+      "mxfp8_e4m3" ("mx_fp8_e4m3")           e4m3 [rows, H] + e8m0 codes uint8 [rows, H/32]
+      "mxfp8_e5m2" ("mx_fp8_e5m2")           e5m2 [rows, H] + e8m0 codes uint8 [rows, H/32]
+      "mxfp4_e2m1" ("mx_fp4_e2m1")           uint8 [rows, H/2], two e2m1 codes per byte
+                                             (low nibble first) + e8m0 uint8 [rows, H/32]"""
     _need(x, "x", torch.bfloat16, 2)
     T, H = x.shape
     idx = layout.topk_idx
     if idx.shape[0] != T:
         raise ValueError("x and topk_idx disagree on the number of tokens")
     K, E = idx.shape[1], layout.num_experts
-    if quant == "bf16":
-        q, rdt = N.EP_QUANT_BF16, torch.bfloat16
-    elif quant == "fp8_e4m3_g128":
-        q, rdt = N.EP_QUANT_FP8_E4M3_G128, torch.float8_e4m3fn
-    else:
+    quant = _QUANT_ALIASES.get(quant, quant)
+    if quant not in _QUANT:
         raise ValueError(f"unknown quant mode {quant!r}")
+    q, rdt, row_div, scale_shape = _QUANT[quant]
     if recv_layout == "contiguous":
         lay, arg = N.EP_LAYOUT_CONTIGUOUS, (T * K if max_rows is None else int(max_rows))
         rows = arg
@@ -128,8 +152,11 @@ def dispatch(x: torch.Tensor, layout: Layout, *, quant: str = "bf16",
     else:
         raise ValueError(f"unknown receive layout {recv_layout!r}")
     dev = x.device
-    recv = torch.empty((rows, H), dtype=rdt, device=dev)
-    scales = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if q else None
+    recv = torch.empty((rows, H // row_div), dtype=rdt, device=dev)
+    scales = None
+    if scale_shape is not None:
+        ncol, sdt = scale_shape(H)
+        scales = torch.empty((rows, ncol) if ncol else (rows,), dtype=sdt, device=dev)
     slot = torch.empty((T, K), dtype=torch.int32, device=dev)
     src = torch.empty(rows, dtype=torch.int32, device=dev)
     nd = torch.empty(1, dtype=torch.int32, device=dev)

@@ -97,7 +97,7 @@ ep_status_t ep_get_dispatch_layout(const int32_t *topk_idx, int T, int K, int E,
 
 ep_status_t ep_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx, int K, int E,
                         const int32_t *offsets, ep_recv_layout_t layout, int cap_or_max_rows,
-                        ep_quant_t quant, void *recv_x, float *recv_scales, int32_t *slot,
+                        ep_quant_t quant, void *recv_x, void *recv_scales, int32_t *slot,
                         int32_t *recv_src, int32_t *num_dropped, void *ws, size_t ws_bytes,
                         void *stream)
 {
@@ -106,28 +106,35 @@ ep_status_t ep_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx
         return st;
     if (layout != EP_LAYOUT_CONTIGUOUS && layout != EP_LAYOUT_PADDED)
         return EP_ERR_INVALID_ARG;
-    if (quant != EP_QUANT_BF16 && quant != EP_QUANT_FP8_E4M3_G128)
+    if ((int)quant < (int)EP_QUANT_BF16 || (int)quant > (int)EP_QUANT_MXFP4_E2M1)
         return EP_ERR_INVALID_ARG;
-    const bool fp8 = quant == EP_QUANT_FP8_E4M3_G128;
+    const bool quantised = quant != EP_QUANT_BF16;
+    const bool mx = quant == EP_QUANT_MXFP8_E4M3 || quant == EP_QUANT_MXFP8_E5M2 ||
+                    quant == EP_QUANT_MXFP4_E2M1;
+    const bool per_token = quant == EP_QUANT_FP8_E4M3_TOKEN || quant == EP_QUANT_INT8_TOKEN;
     const bool padded = layout == EP_LAYOUT_PADDED;
-    if (H < 8 || H % 8 != 0 || (fp8 && H % 128 != 0))
+    if (H < 8 || H % 8 != 0 || (quant == EP_QUANT_FP8_E4M3_G128 && H % 128 != 0) ||
+        (mx && H % 32 != 0))
         return EP_ERR_INVALID_ARG;
+    if (per_token && !ep::dispatch_row_fits_one_block(H))
+        return EP_ERR_UNSUPPORTED;
     if (cap_or_max_rows < 0)
         return EP_ERR_INVALID_ARG;
     const int64_t rows = padded ? (int64_t)E * cap_or_max_rows : cap_or_max_rows;
     if (rows > kI32)
         return EP_ERR_INVALID_ARG;
     if (!offsets || !num_dropped || (T > 0 && (!x || !topk_idx || !slot)) ||
-        (rows > 0 && T > 0 && !recv_x) || (fp8 && rows > 0 && T > 0 && !recv_scales))
+        (rows > 0 && T > 0 && !recv_x) || (quantised && rows > 0 && T > 0 && !recv_scales))
         return EP_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(recv_scales, 4) ||
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || (!mx && !aligned(recv_scales, 4)) ||
         !aligned(topk_idx, 4) || !aligned(offsets, 4) || !aligned(slot, 4) ||
         !aligned(recv_src, 4) || !aligned(num_dropped, 4))
         return EP_ERR_INVALID_ARG;
     ep::LayoutPlan p = ep::make_layout_plan(T, K, E, 1);
     if ((st = check_ws(ws, ws_bytes, p.bytes)) != EP_OK)
         return st;
-    return hip_status(ep::launch_dispatch(p, x, H, topk_idx, offsets, padded, cap_or_max_rows, fp8,
+    return hip_status(ep::launch_dispatch(p, x, H, topk_idx, offsets, padded, cap_or_max_rows,
+                                          (int)quant,
                                           recv_x, recv_scales, slot, recv_src, num_dropped,
                                           static_cast<char *>(ws),
                                           static_cast<hipStream_t>(stream)));

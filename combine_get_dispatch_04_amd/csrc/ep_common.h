@@ -54,6 +54,10 @@ __device__ __forceinline__ void row_st8(rsrc_t r, int off, u32x2 v)
 {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStorePolicy);
 }
+__device__ __forceinline__ void row_st4(rsrc_t r, int off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kStorePolicy);
+}
 __device__ __forceinline__ u32x4 row_ld16(rsrc_t r, int off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy);
@@ -103,6 +107,70 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_rne(float v)
         code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);   // exponent - 127 + 7
     }
     return sign | code;
+}
+
+// fp32 -> OCP E5M2 code (bias 15, 2 mantissa bits, largest finite 57344),
+// round to nearest even, saturating (no infinity is produced).  Below 2^-14
+// the code is the subnormal count round(|v| * 2^16); from 2^-14 up the
+// pattern is rounded to 2 mantissa bits in place and rebiased.  |v| >= 61440
+// (the midpoint above 57344) saturates.
+__device__ __forceinline__ uint32_t f32_to_e5m2_rne(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x47700000u) {                 // 61440.0
+        code = 0x7Bu;
+    } else if (a < 0x38800000u) {           // 2^-14
+        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 65536.0f);
+    } else {
+        uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);
+        code = (((r >> 23) - 112u) << 2) | ((r >> 21) & 3u);   // exponent - 127 + 15
+    }
+    return sign | code;
+}
+
+// fp32 -> OCP E2M1 4-bit code (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 = codes
+// 0..7, bit 3 the sign), round to nearest even, saturating at 6.  Below 1
+// the code is round(|v| * 2) (2 is the code of 1.0); from 1 up the pattern
+// is rounded to one mantissa bit in place and rebiased (bias 1).
+__device__ __forceinline__ uint32_t f32_to_e2m1_rne(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 28) & 0x8u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x40C00000u) {                 // 6.0
+        code = 7u;
+    } else if (a < 0x3F800000u) {           // 1.0
+        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 2.0f);
+    } else {
+        uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
+        code = (((r >> 23) - 126u) << 1) | ((r >> 22) & 1u);   // exponent - 127 + 1
+    }
+    return sign | code;
+}
+
+// fp32 -> int8 code (two's complement byte): round to nearest even, clamped
+// to [-127, 127].
+__device__ __forceinline__ uint32_t f32_to_int8_rne(float v)
+{
+    float r = fminf(fmaxf(__builtin_rintf(v), -127.0f), 127.0f);
+    return (uint32_t)(int)r & 0xFFu;
+}
+
+// Shared exponent of a 32-element MX block: floor(log2(amax)) - emax,
+// clamped to [-127, 127]; an all-zero block gives -127.  floor(log2) is the
+// exponent field, or for an fp32 subnormal the position of the top bit.
+__device__ __forceinline__ int mx_shared_exponent(float amax, int emax)
+{
+    const uint32_t a = __float_as_uint(amax);
+    if (a == 0u)
+        return -127;
+    int e = (a >> 23) ? (int)(a >> 23) - 127 : (31 - (int)__clz(a)) - 149;
+    e -= emax;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
 // ---------------------------------------------------------------- waves

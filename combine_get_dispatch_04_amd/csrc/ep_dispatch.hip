@@ -1,17 +1,23 @@
 // ep_dispatch.hip -- token dispatch into the receive buffer ("DeepEP-Ascend"
 // README, API Overview: dispatch and low_latency_dispatch; Quantization
-// Modes in Normal Dispatch: bf16, or float8_e4m3fn codes with float32
-// scales).
+// Modes in Normal Dispatch: bf16; float8_e4m3fn codes with float32 scales
+// per 128 channels; INT8 dynamic and scalar FP8 with one float32 scale per
+// token; MXFP8 (e4m3 or e5m2) and MXFP4 (e2m1) with a float8_e8m0fnu scale
+// per 32 elements).
 //
 // Token-major: one block per (token, row segment).  The block reads its
-// piece of x[t] once into registers (16 bytes per thread per piece), then
-// for each of the token's K slots computes the receive row from the layout
-// tables and stores the piece there (buffer stores bounded by the row).  The slot arithmetic reads only
-// block-uniform addresses, so it runs on the scalar unit.  fp8 quantises
-// once per token: a 128-channel group is 16 consecutive lanes; its |max| is
-// reduced across them with lane shuffles, the scale is a correctly rounded
-// fp32 division, and every element is divided by it (also correctly
-// rounded) before the round-to-nearest-even e4m3 encoding.
+// piece of x[t] once into registers (16 bytes = 8 channels per thread per
+// piece), quantises it once, then for each of the token's K slots computes
+// the receive row from the layout tables and stores the piece there (buffer
+// stores bounded by the row).  The slot arithmetic reads only block-uniform
+// addresses, so it runs on the scalar unit.
+//
+// Quantisation groups map onto lanes: a 128-channel group is 16 consecutive
+// lanes and a 32-channel MX block 4 lanes, reduced with lane shuffles; a
+// per-token scale needs the whole row in one block (one row segment) and a
+// block reduction.  Scales are correctly rounded fp32 divisions, elements are
+// divided by them (also correctly rounded) or, for MX, multiplied by the
+// exact power of two 2^-E, then encoded with round-to-nearest-even.
 #include "ep_common.h"
 #include "ep_internal.h"
 
@@ -48,15 +54,59 @@ __global__ void dropped_only_kernel(const int32_t *__restrict__ offsets, int E, 
     write_num_dropped(offsets, E, padded, cap_or_rows, num_dropped);
 }
 
-template <int PPT, bool FP8>
+constexpr bool is_token_mode(int m) { return m == kQuantFp8Token || m == kQuantInt8Token; }
+constexpr bool is_mx_mode(int m)
+{
+    return m == kQuantMxE4M3 || m == kQuantMxE5M2 || m == kQuantMxE2M1;
+}
+constexpr int mx_emax(int m) { return m == kQuantMxE4M3 ? 8 : (m == kQuantMxE5M2 ? 15 : 2); }
+
+// Bytes of one receive row.
+__host__ __device__ constexpr int64_t row_bytes(int m, int H)
+{
+    return m == kQuantBf16 ? 2 * (int64_t)H : (m == kQuantMxE2M1 ? H / 2 : (int64_t)H);
+}
+
+template <int MODE>
+__device__ __forceinline__ uint32_t encode(float v)
+{
+    if constexpr (MODE == kQuantInt8Token)
+        return f32_to_int8_rne(v);
+    else if constexpr (MODE == kQuantMxE5M2)
+        return f32_to_e5m2_rne(v);
+    else if constexpr (MODE == kQuantMxE2M1)
+        return f32_to_e2m1_rne(v);
+    else
+        return f32_to_e4m3_rne(v);
+}
+
+// Max of v over the block (blockDim.x <= 256); every thread gets it.
+__device__ __forceinline__ float block_max(float v)
+{
+    __shared__ float red[4];
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, kWave));
+    const int wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
+    if (threadIdx.x % kWave == 0)
+        red[wave] = v;
+    __syncthreads();
+    float m = red[0];
+    for (int w = 1; w < nw; ++w)
+        m = fmaxf(m, red[w]);
+    return m;
+}
+
+template <int PPT, int MODE>
 __global__ void __launch_bounds__(256)
 dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict__ topk_idx, int K,
                 int E, const int32_t *__restrict__ offsets, int padded, int cap_or_rows, int CT,
                 int nchunk, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ local_rank,
-                void *__restrict__ recv_x, float *__restrict__ recv_s,
+                void *__restrict__ recv_x, void *__restrict__ recv_s,
                 int32_t *__restrict__ slot_out, int32_t *__restrict__ recv_src,
                 int32_t *__restrict__ num_dropped)
 {
+    constexpr bool QUANT = MODE != kQuantBf16;
     const int t = blockIdx.x;
     const int tid = threadIdx.x, bd = blockDim.x;
     const int pieces = H >> 3;
@@ -72,45 +122,88 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
         v[j] = i < pieces ? ld16(xrow + (size_t)i * 16) : u32x4{0u, 0u, 0u, 0u};
     }
 
-    u32x2 q[FP8 ? PPT : 1];
-    float sc[FP8 ? PPT : 1];
-    if constexpr (FP8) {
+    // q: the piece's codes (8 bytes, or 4 for e2m1); sc: its group's scale
+    // (fp32 bits for the 128-channel groups, the e8m0 code for MX)
+    u32x2 q[QUANT ? PPT : 1];
+    uint32_t sc[QUANT ? PPT : 1];
+    float tok_scale = 0.0f;
+    if constexpr (QUANT) {
+        // |x| of a (non-NaN) bf16 orders like the integer of its low 15 bits,
+        // so the piece's max comes from the packed bits; channels are decoded
+        // to fp32 only where they are encoded (fewer live registers)
+        float amax[PPT];
 #pragma unroll
         for (int j = 0; j < PPT; ++j) {
-            int i = seg0 + tid + j * bd;
-            float f[8] = {bf16_lo(v[j].x), bf16_hi(v[j].x), bf16_lo(v[j].y), bf16_hi(v[j].y),
-                          bf16_lo(v[j].z), bf16_hi(v[j].z), bf16_lo(v[j].w), bf16_hi(v[j].w)};
+            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+            uint32_t m = 0u;
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+                m = max(m, max(w[h] & 0x7FFFu, (w[h] >> 16) & 0x7FFFu));
+            amax[j] = __uint_as_float(m << 16);      // out-of-row pieces are zeros
+        }
+        if constexpr (is_token_mode(MODE)) {
             float a = 0.0f;
-            if (i < pieces)
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    a = fmaxf(a, fabsf(f[u]));
-            // 16 lanes = one 128-channel group (pieces and blockDim are multiples of 16)
+            for (int j = 0; j < PPT; ++j)
+                a = fmaxf(a, amax[j]);
+            a = block_max(a);                         // the row is in this block: one segment
 #pragma unroll
-            for (int o = 1; o < 16; o <<= 1)
-                a = fmaxf(a, __shfl_xor(a, o, kWave));
-            uint32_t c[8];
-            if (a == 0.0f) {
-                sc[j] = 0.0f;
+            for (int j = 0; j < PPT; ++j)
+                amax[j] = a;
+            tok_scale = a == 0.0f ? 0.0f : a / (MODE == kQuantInt8Token ? 127.0f : 448.0f);
+        }
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    c[u] = 0u;
-            } else {
-                float s = a / 448.0f;
-                sc[j] = s;
+        for (int j = 0; j < PPT; ++j) {
+            float a = amax[j];
+            if constexpr (MODE == kQuantFp8G128) {
+                // 16 lanes = one 128-channel group (pieces and blockDim are multiples of 16)
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    c[u] = f32_to_e4m3_rne(f[u] / s);
+                for (int o = 1; o < 16; o <<= 1)
+                    a = fmaxf(a, __shfl_xor(a, o, kWave));
+            } else if constexpr (is_mx_mode(MODE)) {
+                // 4 lanes = one 32-channel block (pieces and blockDim are multiples of 4)
+                a = fmaxf(a, __shfl_xor(a, 1, kWave));
+                a = fmaxf(a, __shfl_xor(a, 2, kWave));
             }
-            q[j].x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-            q[j].y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+            const float f[8] = {bf16_lo(v[j].x), bf16_hi(v[j].x), bf16_lo(v[j].y),
+                                bf16_hi(v[j].y), bf16_lo(v[j].z), bf16_hi(v[j].z),
+                                bf16_lo(v[j].w), bf16_hi(v[j].w)};
+            uint32_t c[8];
+            if constexpr (is_mx_mode(MODE)) {
+                const int e = mx_shared_exponent(a, mx_emax(MODE));
+                // 2^-e as an fp32 pattern: e >= -127, and e <= 127 - emax for
+                // finite bf16 input, so 127 - e lies in [2, 254]: a normal number
+                const float m = __uint_as_float((uint32_t)(127 - e) << 23);
+                sc[j] = (uint32_t)(e + 127);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    c[u] = encode<MODE>(f[u] * m);
+            } else {
+                const float s = MODE == kQuantFp8G128 ? (a == 0.0f ? 0.0f : a / 448.0f) : tok_scale;
+                sc[j] = __float_as_uint(s);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    c[u] = s == 0.0f ? 0u : encode<MODE>(f[u] / s);
+            }
+            if constexpr (MODE == kQuantMxE2M1) {
+                q[j].x = c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12) | (c[4] << 16) |
+                         (c[5] << 20) | (c[6] << 24) | (c[7] << 28);
+                q[j].y = 0u;
+            } else {
+                q[j].x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+                q[j].y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+            }
+            // keep the packed words here: left to itself the compiler sinks
+            // the packing into the slot loop and keeps all 8 codes of every
+            // piece live (131 VGPRs instead of about 60 at 7 pieces)
+            asm volatile("" : "+v"(q[j].x), "+v"(q[j].y), "+v"(sc[j]));
         }
     }
 
     const int c = t / CT;
     const int32_t *trow = topk_idx + (int64_t)t * K;
     const int32_t *rrow = local_rank + (int64_t)t * K;
-    const int G = H >> 7;
+    const int64_t rb = row_bytes(MODE, H);
     for (int k = 0; k < K; ++k) {
         const int e = trow[k];
         int s = -1;
@@ -131,21 +224,33 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
         }
         if (s < 0)
             continue;
-        if constexpr (FP8) {
-            const rsrc_t dst = row_rsrc(reinterpret_cast<char *>(recv_x) + (size_t)s * H, H);
-            float *sdst = recv_s + (size_t)s * G;
-#pragma unroll
-            for (int j = 0; j < PPT; ++j) {
-                int i = seg0 + tid + j * bd;
-                row_st8(dst, i * 8, q[j]);
-                if ((tid & 15) == 0 && i < pieces)
-                    sdst[i >> 4] = sc[j];
-            }
-        } else {
-            const rsrc_t dst = row_rsrc(reinterpret_cast<char *>(recv_x) + (size_t)s * H * 2, H * 2);
+        const rsrc_t dst = row_rsrc(reinterpret_cast<char *>(recv_x) + (size_t)s * rb, (int)rb);
+        if constexpr (!QUANT) {
 #pragma unroll
             for (int j = 0; j < PPT; ++j)
                 row_st16(dst, (seg0 + tid + j * bd) * 16, v[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < PPT; ++j) {
+                const int i = seg0 + tid + j * bd;
+                if constexpr (MODE == kQuantMxE2M1)
+                    row_st4(dst, i * 4, q[j].x);
+                else
+                    row_st8(dst, i * 8, q[j]);
+                if constexpr (MODE == kQuantFp8G128) {
+                    if ((tid & 15) == 0 && i < pieces)
+                        reinterpret_cast<float *>(recv_s)[(size_t)s * (H >> 7) + (i >> 4)] =
+                            __uint_as_float(sc[j]);
+                } else if constexpr (is_mx_mode(MODE)) {
+                    if ((tid & 3) == 0 && i < pieces)
+                        reinterpret_cast<uint8_t *>(recv_s)[(size_t)s * (H >> 5) + (i >> 2)] =
+                            (uint8_t)sc[j];
+                }
+            }
+            if constexpr (is_token_mode(MODE)) {
+                if (tid == 0)
+                    reinterpret_cast<float *>(recv_s)[s] = tok_scale;
+            }
         }
     }
 }
@@ -179,20 +284,21 @@ RowShape row_shape(int pieces)
     return best;
 }
 
-template <bool FP8>
+template <int MODE>
 hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint16_t *x, int H,
                              const int32_t *topk_idx, const int32_t *offsets, int padded,
-                             int cap_or_rows, void *recv_x, float *recv_s, int32_t *slot,
+                             int cap_or_rows, void *recv_x, void *recv_s, int32_t *slot,
                              int32_t *recv_src, int32_t *num_dropped, const int32_t *hist,
                              const int32_t *rank, hipStream_t s)
 {
+    if (is_token_mode(MODE) && rs.nseg != 1)      // the host checks H first
+        return hipErrorInvalidValue;
     dim3 grid(p.T, rs.nseg), block(rs.bd);
-#define EP_DISPATCH_CASE(N)                                                                     \
-    case N:                                                                                     \
-        hipLaunchKernelGGL((dispatch_kernel<N, FP8>), grid, block, 0, s, x, H, topk_idx, p.K, \
-                           p.E, offsets, padded, cap_or_rows, p.CT, p.nchunk, hist, rank,      \
-                           recv_x, recv_s,                                                      \
-                           slot, recv_src, num_dropped);                                        \
+#define EP_DISPATCH_CASE(N)                                                                      \
+    case N:                                                                                      \
+        hipLaunchKernelGGL((dispatch_kernel<N, MODE>), grid, block, 0, s, x, H, topk_idx, p.K, \
+                           p.E, offsets, padded, cap_or_rows, p.CT, p.nchunk, hist, rank,       \
+                           recv_x, recv_s, slot, recv_src, num_dropped);                         \
         break;
     switch (rs.ppt) {
         EP_DISPATCH_CASE(1)
@@ -212,9 +318,11 @@ hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint
 
 }  // namespace
 
+bool dispatch_row_fits_one_block(int H) { return row_shape(H / 8).nseg == 1; }
+
 hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const int32_t *topk_idx,
-                           const int32_t *offsets, bool padded, int cap_or_rows, bool fp8,
-                           void *recv_x, float *recv_scales, int32_t *slot, int32_t *recv_src,
+                           const int32_t *offsets, bool padded, int cap_or_rows, int quant,
+                           void *recv_x, void *recv_scales, int32_t *slot, int32_t *recv_src,
                            int32_t *num_dropped, char *ws, hipStream_t s)
 {
     const int32_t *hist = reinterpret_cast<const int32_t *>(ws + p.off_hist);
@@ -225,11 +333,22 @@ hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const 
         return hipGetLastError();
     }
     RowShape rs = row_shape(H / 8);
-    if (fp8)
-        return launch_dispatch_t<true>(p, rs, x, H, topk_idx, offsets, padded, cap_or_rows, recv_x,
-                                       recv_scales, slot, recv_src, num_dropped, hist, rank, s);
-    return launch_dispatch_t<false>(p, rs, x, H, topk_idx, offsets, padded, cap_or_rows, recv_x,
+#define EP_MODE_CASE(M)                                                                          \
+    case M:                                                                                      \
+        return launch_dispatch_t<M>(p, rs, x, H, topk_idx, offsets, padded, cap_or_rows, recv_x, \
                                     recv_scales, slot, recv_src, num_dropped, hist, rank, s);
+    switch (quant) {
+        EP_MODE_CASE(kQuantBf16)
+        EP_MODE_CASE(kQuantFp8G128)
+        EP_MODE_CASE(kQuantFp8Token)
+        EP_MODE_CASE(kQuantInt8Token)
+        EP_MODE_CASE(kQuantMxE4M3)
+        EP_MODE_CASE(kQuantMxE5M2)
+        EP_MODE_CASE(kQuantMxE2M1)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef EP_MODE_CASE
 }
 
 }  // namespace ep

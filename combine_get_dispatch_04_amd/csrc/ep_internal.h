@@ -33,9 +33,22 @@ hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *
                          int32_t *offsets, int32_t *tokens_per_rank, uint8_t *is_token_in_rank,
                          int32_t *num_invalid, char *ws, hipStream_t s);
 
+// Quantisation modes; the values are those of ep_quant_t.
+constexpr int kQuantBf16 = 0;
+constexpr int kQuantFp8G128 = 1;
+constexpr int kQuantFp8Token = 2;
+constexpr int kQuantInt8Token = 3;
+constexpr int kQuantMxE4M3 = 4;
+constexpr int kQuantMxE5M2 = 5;
+constexpr int kQuantMxE2M1 = 6;
+
+// True when a row of H channels is handled by one dispatch block (needed by
+// the per-token modes, whose scale is a reduction over the row).
+bool dispatch_row_fits_one_block(int H);
+
 hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const int32_t *topk_idx,
-                           const int32_t *offsets, bool padded, int cap_or_rows, bool fp8,
-                           void *recv_x, float *recv_scales, int32_t *slot, int32_t *recv_src,
+                           const int32_t *offsets, bool padded, int cap_or_rows, int quant,
+                           void *recv_x, void *recv_scales, int32_t *slot, int32_t *recv_src,
                            int32_t *num_dropped, char *ws, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot,

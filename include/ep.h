@@ -58,8 +58,13 @@ typedef enum {
 } ep_recv_layout_t;
 
 typedef enum {
-    EP_QUANT_BF16 = 0,          /* rows copied as bf16 */
-    EP_QUANT_FP8_E4M3_G128 = 1  /* e4m3 codes + one fp32 scale per 128 channels */
+    EP_QUANT_BF16 = 0,           /* rows copied as bf16 */
+    EP_QUANT_FP8_E4M3_G128 = 1,  /* e4m3 codes + one fp32 scale per 128 channels */
+    EP_QUANT_FP8_E4M3_TOKEN = 2, /* e4m3 codes + one fp32 scale per token ("pertoken_fp8_e4m3") */
+    EP_QUANT_INT8_TOKEN = 3,     /* int8 codes + one fp32 scale per token ("int8") */
+    EP_QUANT_MXFP8_E4M3 = 4,     /* e4m3 codes + one e8m0 scale per 32 channels ("mx_fp8_e4m3") */
+    EP_QUANT_MXFP8_E5M2 = 5,     /* e5m2 codes + one e8m0 scale per 32 channels ("mx_fp8_e5m2") */
+    EP_QUANT_MXFP4_E2M1 = 6      /* e2m1 codes, 2 per byte, + e8m0 per 32 ("mx_fp4_e2m1") */
 } ep_quant_t;
 
 /* Human-readable name of a status code (static string). */
@@ -101,7 +106,9 @@ ep_status_t ep_get_dispatch_layout(const int32_t *topk_idx, int T, int K, int E,
 /*
  * ep_dispatch -- [EPA] API Overview, dispatch (contiguous receive buffer)
  * and low_latency_dispatch (per-expert capacity); [EPA] Quantization Modes
- * (bf16, or float8_e4m3fn with float32 scales).
+ * in Normal Dispatch (bf16; INT8 dynamic and scalar FP8 per token with
+ * float32 scales; MXFP8 e4m3/e5m2 and MXFP4 e2m1 with float8_e8m0fnu scales
+ * per 32 elements), plus e4m3 with a float32 scale per 128 channels.
  *
  * The receive row ("slot") of a valid (t,k) with expert e is found by a
  * stable counting sort: r = number of valid (t',k') before (t,k) in
@@ -120,11 +127,34 @@ ep_status_t ep_get_dispatch_layout(const int32_t *topk_idx, int T, int K, int E,
  *                           a == 0); recv_x[slot, :] = q (uint8 [rows, H]),
  *                           recv_scales[slot, g] = s (fp32 [rows, H/128]).
  *                           Needs H % 128 == 0.
+ *   EP_QUANT_FP8_E4M3_TOKEN, EP_QUANT_INT8_TOKEN: the same with one group per
+ *                           token: a = max|x| over the row, s = a / 448
+ *                           (e4m3) or a / 127 (int8: q = x / s rounded to
+ *                           nearest even, clamped to [-127, 127], stored as
+ *                           two's complement bytes); recv_x uint8 [rows, H],
+ *                           recv_scales fp32 [rows].  Needs H <= 16384
+ *                           (EP_ERR_UNSUPPORTED beyond: the row must fit one
+ *                           block).
+ *   EP_QUANT_MXFP8_E4M3, EP_QUANT_MXFP8_E5M2, EP_QUANT_MXFP4_E2M1: per token
+ *                           and 32-channel block b, with a = max|x| over the
+ *                           block: E = floor(log2(a)) - emax (emax = 8, 15,
+ *                           2), clamped to [-127, 127], E = -127 when a == 0;
+ *                           recv_scales[slot, b] = E + 127 (e8m0 code, uint8
+ *                           [rows, H/32]); element = x * 2^-E (exact)
+ *                           rounded to nearest even in the element format,
+ *                           saturating at its largest finite value (448,
+ *                           57344, 6).  recv_x is uint8 [rows, H] (fp8) or
+ *                           [rows, H/2] (e2m1: channel 2i in the low nibble
+ *                           of byte i, 2i+1 in the high nibble).  Needs
+ *                           H % 32 == 0.
  *   x            [T, H] bf16 in.
  *   topk_idx     [T, K] int32 in (the array given to ep_get_dispatch_layout).
  *   offsets      [E+1] int32 in, from ep_get_dispatch_layout.
- *   recv_x       [rows, H] out; rows that receive no token are not written.
- *   recv_scales  [rows, H/128] fp32 out (fp8 only; NULL for bf16).
+ *   recv_x       [rows, row bytes] out (row bytes: 2H bf16, H for the 8-bit
+ *                codes, H/2 for e2m1); rows that receive no token are not
+ *                written.
+ *   recv_scales  out, as given for each mode above (NULL for bf16): fp32
+ *                aligned to 4 bytes, e8m0 codes any alignment.
  *   slot         [T, K] int32 out: the handle for ep_combine.
  *   recv_src     [rows] int32 out or NULL: recv_src[slot] = t for kept slots;
  *                other entries are not written.
@@ -133,7 +163,7 @@ ep_status_t ep_get_dispatch_layout(const int32_t *topk_idx, int T, int K, int E,
  */
 ep_status_t ep_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx, int K, int E,
                         const int32_t *offsets, ep_recv_layout_t layout, int cap_or_max_rows,
-                        ep_quant_t quant, void *recv_x, float *recv_scales,
+                        ep_quant_t quant, void *recv_x, void *recv_scales,
                         int32_t *slot, int32_t *recv_src, int32_t *num_dropped,
                         void *ws, size_t ws_bytes, void *stream);
 

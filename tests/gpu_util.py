@@ -51,15 +51,33 @@ def layout(idx_d: torch.Tensor, E: int, R: int = 1, with_rank=True):
     return out
 
 
-def dispatch(x_d, idx_d, E, L, padded=False, cap_or_rows=None, fp8=False, sentinel=True):
+SENT_E8M0 = 0xEE     # an e8m0 code only for block maxima of 2^111 and above (not in the tests)
+
+
+def quant_buffers(quant, rows, H, sentinel=True):
+    """Receive payload and scale arrays of ep_quant_t `quant` (>= 1), filled
+    with sentinels."""
+    rb = H // 2 if quant == N.EP_QUANT_MXFP4_E2M1 else H
+    recv = torch.full((rows, rb), SENT8 if sentinel else 0, dtype=torch.uint8, device=DEV)
+    if quant == N.EP_QUANT_FP8_E4M3_G128:
+        sc = torch.full((rows, H // 128), -1.0, dtype=torch.float32, device=DEV)
+    elif quant in (N.EP_QUANT_FP8_E4M3_TOKEN, N.EP_QUANT_INT8_TOKEN):
+        sc = torch.full((max(rows, 1),), -1.0, dtype=torch.float32, device=DEV)
+    else:
+        sc = torch.full((rows, H // 32), SENT_E8M0, dtype=torch.uint8, device=DEV)
+    return recv, sc
+
+
+def dispatch(x_d, idx_d, E, L, padded=False, cap_or_rows=None, fp8=False, sentinel=True, quant=None):
     T, H = x_d.shape
     K = idx_d.shape[1]
     if cap_or_rows is None:
         cap_or_rows = T * K
     rows = E * cap_or_rows if padded else cap_or_rows
-    if fp8:
-        recv = torch.full((rows, H), SENT8 if sentinel else 0, dtype=torch.uint8, device=DEV)
-        sc = torch.full((rows, H // 128), -1.0, dtype=torch.float32, device=DEV)
+    if quant is None:
+        quant = N.EP_QUANT_FP8_E4M3_G128 if fp8 else N.EP_QUANT_BF16
+    if quant != N.EP_QUANT_BF16:
+        recv, sc = quant_buffers(quant, rows, H, sentinel)
     else:
         recv = torch.full((rows, H), SENT16 if sentinel else 0, dtype=torch.int16,
                           device=DEV).view(torch.bfloat16)
@@ -68,7 +86,7 @@ def dispatch(x_d, idx_d, E, L, padded=False, cap_or_rows=None, fp8=False, sentin
     src = torch.full((max(rows, 1),), -2, dtype=torch.int32, device=DEV)
     nd = torch.full((1,), -7, dtype=torch.int32, device=DEV)
     N.ep_dispatch(p(x_d), T, H, p(idx_d), K, E, p(L["offsets"]), int(padded), cap_or_rows,
-                  int(fp8), p(recv), p(sc), p(slot), p(src), p(nd), p(L["ws"]), L["ws"].numel(),
+                  int(quant), p(recv), p(sc), p(slot), p(src), p(nd), p(L["ws"]), L["ws"].numel(),
                   stream())
     return recv, sc, slot, src, nd
 
