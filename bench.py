@@ -73,9 +73,106 @@ class Path:
         self.alg_bytes, self.meta = alg_bytes, meta
 
 
+# quant name -> (ep_quant_t attribute, bytes of a receive row, scale shape)
+# where the scale shape maps H to (columns or 0 for one per row, numpy-like
+# dtype name), or None for bf16
+QUANT_MODES = {
+    "bf16": ("EP_QUANT_BF16", lambda H: 2 * H, None),
+    "fp8_e4m3_g128": ("EP_QUANT_FP8_E4M3_G128", lambda H: H + 4 * (H // 128),
+                      lambda H: (H // 128, "float32")),
+    "fp8_e4m3_token": ("EP_QUANT_FP8_E4M3_TOKEN", lambda H: H + 4, lambda H: (0, "float32")),
+    "int8_token": ("EP_QUANT_INT8_TOKEN", lambda H: H + 4, lambda H: (0, "float32")),
+    "mxfp8_e4m3": ("EP_QUANT_MXFP8_E4M3", lambda H: H + H // 32, lambda H: (H // 32, "uint8")),
+    "mxfp8_e5m2": ("EP_QUANT_MXFP8_E5M2", lambda H: H + H // 32, lambda H: (H // 32, "uint8")),
+    "mxfp4_e2m1": ("EP_QUANT_MXFP4_E2M1", lambda H: H // 2 + H // 32,
+                   lambda H: (H // 32, "uint8")),
+}
+
+
+def dequantise(torch, recv, scales, quant, H):
+    """bf16 rows from the receive buffer (identity experts), with torch
+    element casts; run once, outside the timed region."""
+    if quant == "bf16":
+        return recv
+    f8 = {"fp8_e4m3_g128": torch.float8_e4m3fn, "fp8_e4m3_token": torch.float8_e4m3fn,
+          "mxfp8_e4m3": torch.float8_e4m3fn, "mxfp8_e5m2": torch.float8_e5m2}
+    if quant == "int8_token":
+        v = recv.view(torch.int8).float()
+    elif quant == "mxfp4_e2m1":
+        lut = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                            -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0], device=recv.device)
+        b = recv.view(torch.uint8).long()
+        v = torch.stack([lut[b & 15], lut[b >> 4]], dim=-1).reshape(recv.shape[0], H)
+    else:
+        v = recv.view(f8[quant]).float()
+    if quant == "fp8_e4m3_g128":
+        v = v * scales.repeat_interleave(128, dim=1)
+    elif quant in ("fp8_e4m3_token", "int8_token"):
+        v = v * scales[:, None]
+    else:
+        v = v * torch.exp2(scales.float() - 127.0).repeat_interleave(32, dim=1)
+    return v.to(torch.bfloat16)
+
+
+def chunked_token_choice_path(c, N, torch, dev, sp, chunk):
+    """The same step in rounds of at most `chunk` tokens (long-sequence
+    chunking): each round runs layout, dispatch and combine on its slice of
+    tokens, reusing one receive buffer of chunk*K rows and one workspace."""
+    T, H, E, K = c.T, c.H, c.E, c.K
+    if c.quant != "bf16" or c.layout != "contiguous":
+        raise SystemExit("--chunk is measured for the bf16 contiguous layout")
+    P = lambda t: t.data_ptr() if t is not None else None
+    x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    idx = torch.from_numpy(c.topk_idx).to(dev)
+    w = torch.from_numpy(c.topk_weights).to(dev)
+    n_valid = int(((c.topk_idx >= 0) & (c.topk_idx < E)).sum())
+    ws_bytes = N.ep_workspace_bytes(min(chunk, T), K, E, 1)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    tpr = torch.empty(1, dtype=torch.int32, device=dev)
+    itr = torch.empty((min(chunk, T), 1), dtype=torch.uint8, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    rows = min(chunk, T) * K
+    recv = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    slot = torch.empty((min(chunk, T), K), dtype=torch.int32, device=dev)
+    src = torch.empty(rows, dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ops = []
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        n = t1 - t0
+        xs, ids, ws_, outs = x[t0:t1], idx[t0:t1], w[t0:t1], out[t0:t1]
+
+        def layout(ids=ids, n=n):
+            N.ep_get_dispatch_layout(P(ids), n, K, E, 1, P(counts), P(offsets), P(tpr), P(itr),
+                                     P(ninv), P(ws), ws_bytes, sp)
+
+        def dispatch(xs=xs, ids=ids, n=n):
+            N.ep_dispatch(P(xs), n, H, P(ids), K, E, P(offsets), N.EP_LAYOUT_CONTIGUOUS, n * K,
+                          N.EP_QUANT_BF16, P(recv), None, P(slot), P(src), P(nd), P(ws),
+                          ws_bytes, sp)
+
+        def combine(ws_=ws_, outs=outs, n=n):
+            N.ep_combine(P(recv), n * K, H, P(slot), P(ws_), n, K, P(outs), sp)
+
+        ops += [("layout", layout), ("dispatch", dispatch), ("combine", combine)]
+    alg = {"layout": T * K * 4,
+           "dispatch": T * H * 2 + n_valid * 2 * H + 2 * T * K * 4,
+           "combine": n_valid * H * 2 + T * H * 2 + 2 * T * K * 4}
+    kern = {"layout": "layout_chunk_kernel", "dispatch": "dispatch_kernel",
+            "combine": "combine_kernel"}
+    meta = {"T": T, "H": H, "E": E, "top_k": K, "recv_layout": "contiguous", "quant": "bf16",
+            "combine": "weighted", "valid_slots": n_valid, "chunk_tokens": chunk,
+            "rounds": (T + chunk - 1) // chunk, "receive_rows": rows}
+    return Path(c.name, T, ops, kern, alg, meta)
+
+
 def token_choice_path(c, N, torch, dev, sp):
     T, H, E, K = c.T, c.H, c.E, c.K
-    fp8 = c.quant == "fp8_e4m3_g128"
+    quant = c.quant
+    qname, row_bytes, scale_shape = QUANT_MODES[quant]
     padded = c.layout == "padded"
     cap_or_rows = c.cap if padded else T * K
     rows = E * c.cap if padded else T * K
@@ -91,13 +188,20 @@ def token_choice_path(c, N, torch, dev, sp):
     tpr = torch.empty(1, dtype=torch.int32, device=dev)
     itr = torch.empty((T, 1), dtype=torch.uint8, device=dev)
     ninv = torch.empty(1, dtype=torch.int32, device=dev)
-    recv = torch.empty((rows, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
-    scales = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+    if quant == "bf16":
+        recv = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+        scales = None
+    else:
+        recv = torch.empty((rows, H // 2 if quant == "mxfp4_e2m1" else H), dtype=torch.uint8,
+                           device=dev)
+        ncol, sdt = scale_shape(H)
+        scales = torch.empty((rows, ncol) if ncol else (rows,), dtype=getattr(torch, sdt),
+                             device=dev)
     slot = torch.empty((T, K), dtype=torch.int32, device=dev)
     src = torch.empty(rows, dtype=torch.int32, device=dev)
     nd = torch.empty(1, dtype=torch.int32, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    quant = N.EP_QUANT_FP8_E4M3_G128 if fp8 else N.EP_QUANT_BF16
+    qcode = getattr(N, qname)
     lay = N.EP_LAYOUT_PADDED if padded else N.EP_LAYOUT_CONTIGUOUS
 
     def layout():
@@ -105,16 +209,15 @@ def token_choice_path(c, N, torch, dev, sp):
                                  P(ninv), P(ws), ws_bytes, sp)
 
     def dispatch():
-        N.ep_dispatch(P(x), T, H, P(idx), K, E, P(offsets), lay, cap_or_rows, quant, P(recv),
+        N.ep_dispatch(P(x), T, H, P(idx), K, E, P(offsets), lay, cap_or_rows, qcode, P(recv),
                       P(scales), P(slot), P(src), P(nd), P(ws), ws_bytes, sp)
 
-    if fp8:
+    if quant != "bf16":
         # identity expert on the dequantised rows, built once outside the timed region
         layout()
         dispatch()
         torch.cuda.synchronize()
-        y = (recv.view(torch.float8_e4m3fn).float()
-             * scales.repeat_interleave(128, dim=1)).to(torch.bfloat16)
+        y = dequantise(torch, recv, scales, quant, H)
         torch.cuda.synchronize()
     else:
         y = recv
@@ -122,13 +225,12 @@ def token_choice_path(c, N, torch, dev, sp):
     def combine():
         N.ep_combine(P(y), rows, H, P(slot), P(w), T, K, P(out), sp)
 
-    row_in = H + 4 * (H // 128) if fp8 else H * 2
     alg = {"layout": T * K * 4,
-           "dispatch": T * H * 2 + n_valid * row_in + 2 * T * K * 4,
+           "dispatch": T * H * 2 + n_valid * row_bytes(H) + 2 * T * K * 4,
            "combine": n_valid * H * 2 + T * H * 2 + 2 * T * K * 4}
     kern = {"layout": "layout_chunk_kernel",
             "dispatch": "dispatch_kernel", "combine": "combine_kernel"}
-    meta = {"T": T, "H": H, "E": E, "top_k": K, "recv_layout": c.layout, "quant": c.quant,
+    meta = {"T": T, "H": H, "E": E, "top_k": K, "recv_layout": c.layout, "quant": quant,
             "cap": c.cap, "combine": "weighted", "valid_slots": n_valid}
     return Path(c.name, T, [("layout", layout), ("dispatch", dispatch), ("combine", combine)],
                 kern, alg, meta)
@@ -184,11 +286,16 @@ def cpu_baseline(c, budget_s):
             rows = c.E * c.cap if padded else c.T * c.K
             oracle.layout(c.topk_idx, c.E)
             slot, _, _ = oracle.slots(c.topk_idx, c.E, padded, cap)
-            if c.quant == "fp8_e4m3_g128":
-                oracle.dispatch_fp8(c.x, slot, rows)
-                y = np.zeros((rows, c.H), np.uint16)
-            else:
+            if c.quant == "bf16":
                 y = oracle.dispatch_bf16(c.x, slot, rows)
+            else:
+                if c.quant == "fp8_e4m3_g128":
+                    oracle.dispatch_fp8(c.x, slot, rows)
+                elif c.quant in oracle.TOKEN_FMT:
+                    oracle.dispatch_token_quant(c.x, slot, rows, c.quant)
+                else:
+                    oracle.dispatch_mx(c.x, slot, rows, c.quant)
+                y = np.zeros((rows, c.H), np.uint16)
             oracle.combine(y, slot, c.topk_weights)
             what = "layout, slots, dispatch, weighted combine"
         reps += 1
@@ -206,7 +313,13 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "toy", "decode", "expert_choice", "large_padded"])
+                    choices=["prefill", "toy", "decode", "expert_choice", "large_padded", "expert_choice_tc"])
+    ap.add_argument("--quant", default=None, choices=sorted(QUANT_MODES),
+                    help="dispatch quantisation of a token-choice workload (default: the "
+                         "workload's own: bf16, or fp8_e4m3_g128 for decode)")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="run a token-choice step in rounds of at most this many tokens "
+                         "(0 = one round)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--flush-mib", type=int, default=1024,
@@ -229,8 +342,15 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     c = W.WORKLOADS[a.workload]()
+    if a.quant is not None:
+        if a.workload == "expert_choice":
+            print("--quant applies to token-choice workloads only", file=sys.stderr)
+            sys.exit(2)
+        c.quant = a.quant
     if a.workload == "expert_choice":
         path = expert_choice_path(c, N, torch, dev, sp)
+    elif a.chunk > 0:
+        path = chunked_token_choice_path(c, N, torch, dev, sp, a.chunk)
     else:
         path = token_choice_path(c, N, torch, dev, sp)
     flush = torch.empty(a.flush_mib << 20, dtype=torch.uint8, device=dev) if a.flush_mib else None
@@ -275,8 +395,11 @@ def main():
             fn()
         e[nops].record(stream)
     torch.cuda.synchronize()
-    op_us = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]) * 1e3)
-             for j, (name, _) in enumerate(path.ops)}
+    op_us, launches = {}, {}
+    for j, (name, _) in enumerate(path.ops):       # a chunked step repeats each name
+        op_us[name] = op_us.get(name, 0.0) + float(
+            np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]) * 1e3)
+        launches[name] = launches.get(name, 0) + 1
     step_ev = np.array([e[0].elapsed_time(e[nops]) for e in ev]) * 1e3
 
     # cold pass: before each step (outside its events) write flush_mib MiB of
@@ -301,12 +424,16 @@ def main():
 
     alg_total = sum(path.alg_bytes.values())
     dom = max(("dispatch", "combine"), key=lambda n: op_us[n])
-    dom_us, dom_bytes = op_us[dom], path.alg_bytes[dom]
+    dom_us, dom_bytes = op_us[dom] / launches[dom], path.alg_bytes[dom] / launches[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    headline = a.workload == "prefill"
+    headline = (a.workload == "prefill" and path.meta.get("quant") == "bf16"
+                and "chunk_tokens" not in path.meta)
     res = {
         "metric": HEADLINE_METRIC if headline else
-                  f"dispatch+combine tokens/s & achieved HBM GB/s, {c.name}",
+                  f"dispatch+combine tokens/s & achieved HBM GB/s, {c.name}"
+                  + (f" ({path.meta['quant']})" if path.meta.get("quant", "bf16") != "bf16" else "")
+                  + (f" (rounds of {path.meta['chunk_tokens']} tokens)"
+                     if "chunk_tokens" in path.meta else ""),
         "value": path.T / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -316,7 +443,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 dispatch, bf16 combine" if a.workload == "decode" else "bf16",
+        "dtype": "bf16" if path.meta.get("quant", "bf16") == "bf16" else
+                 f"{path.meta['quant']} dispatch, bf16 combine",
         "data": "synthetic",
         "config": {"workload": c.name, **path.meta},
         "achieved_GBps": alg_total / (ms_per_step * 1e-3) / 1e9,

@@ -183,6 +183,40 @@ def combine(y: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor
     return out
 
 
+def dispatch_combine_chunked(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, *,
+                             chunk: int, topk_weights: Optional[torch.Tensor] = None,
+                             expert=None, quant: str = "bf16", num_ranks: int = 1,
+                             keep_rounds: bool = False):
+    """Long prefill in rounds of at most `chunk` tokens ("DeepSeek-V4 昇腾
+    NPU 推理部署实践", custom_params: moe_chunk_max_len bounds the tokens an
+    MoE layer handles at once, against running out of memory on long
+    sequences).  Each round runs layout, dispatch, `expert` and combine on
+    its own slice of tokens, so a receive buffer holds chunk*K rows instead of
+    T*K.  `expert(recv, scales, layout) -> y` maps the received rows to the
+    bf16 rows combine reads (default: identity, bf16 only).  Results equal
+    the unchunked call: a token's rows and their order do not depend on the
+    other tokens of its round.  -> out [T, H], plus the per-round (layout,
+    handle) pairs when keep_rounds is set."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    if expert is None and quant != "bf16":
+        raise ValueError("a quantised dispatch needs an expert that returns bf16 rows")
+    T = x.shape[0]
+    out = torch.empty_like(x)
+    rounds = []
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        L = get_dispatch_layout(topk_idx[t0:t1], num_experts, num_ranks)
+        recv, scales, h = dispatch(x[t0:t1], L, quant=quant)
+        y = recv if expert is None else expert(recv, scales, L)
+        combine(y, h, None if topk_weights is None else topk_weights[t0:t1], out=out[t0:t1])
+        if keep_rounds:
+            rounds.append((L, h))
+    return (out, rounds) if keep_rounds else out
+
+
 def dispatch_expert_choice(x: torch.Tensor, token_indices: torch.Tensor, weights: torch.Tensor):
     """-> (recv_x [E, C, H], ExpertChoiceHandle).  The weights are kept in the
     handle and applied by combine_expert_choice."""

@@ -168,8 +168,41 @@ def large_padded(seed: int = 5) -> TokenChoice:
                              zipf_s=1.1, zipf_coef=1.0, mask_frac=0.15)
 
 
+def as_token_choice(c: ExpertChoice) -> TokenChoice:
+    """The token-centric form of an expert-choice workload, as a caller of a
+    [T, K] API must build it ("[Feature Request] Support Expert-Choice
+    Routing via Native Expert-Centric API", Current Limitation, item 2):
+    topk_idx [T, K] lists the experts that picked each token in ascending
+    order (ascending flat entry e*C + c), padded with -1 to K = the largest
+    number of picks of any token; topk_weights carries each pick's weight
+    and 0 on padding.  Host-side, outside any timed region."""
+    T, E, C = c.T, c.E, c.C
+    flat = c.token_indices.ravel()
+    j = np.nonzero((flat >= 0) & (flat < T))[0]          # valid entries, ascending
+    tok = flat[j].astype(np.int64)
+    order = np.argsort(tok, kind="stable")               # by token, then ascending j
+    j, tok = j[order], tok[order]
+    m = np.bincount(tok, minlength=T)
+    K = max(int(m.max()) if m.size else 0, 1)
+    start = np.concatenate([[0], np.cumsum(m)[:-1]])
+    k = np.arange(j.size) - start[tok]                   # rank inside the token
+    idx = np.full((T, K), -1, np.int32)
+    w = np.zeros((T, K), np.float32)
+    idx[tok, k] = (j // C).astype(np.int32)
+    w[tok, k] = c.weights.ravel()[j]
+    return TokenChoice(name=f"{c.name}_as_token_choice_K{K}", T=T, H=c.H, E=E, K=K, x=c.x,
+                       topk_idx=idx, topk_weights=w, layout="contiguous", quant="bf16",
+                       meta={"from_expert_choice": c.name, "valid_entries": int(j.size)})
+
+
+def expert_choice_tc() -> TokenChoice:
+    """The expert-choice workload in token-centric form ([T, 64], mostly -1)."""
+    return as_token_choice(expert_choice())
+
+
 WORKLOADS = {"toy": toy, "decode": decode, "prefill": prefill,
-             "expert_choice": expert_choice, "large_padded": large_padded}
+             "expert_choice": expert_choice, "large_padded": large_padded,
+             "expert_choice_tc": expert_choice_tc}
 
 
 # Small random cases for parity sweeps: duplicates, -1 padding and invalid

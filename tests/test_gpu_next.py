@@ -1,0 +1,133 @@
+"""GPU parity of two uses of the token-choice path.
+
+* Expert choice emulated through the [T, K] API ("[Feature Request] Support
+  Expert-Choice Routing via Native Expert-Centric API", Current Limitation,
+  item 2): topk_idx lists each token's experts, padded with -1 to the largest
+  pick count.  Both paths sum a token's rows in ascending expert order with
+  fp32 FMAs from +0, so with identity experts the combine outputs must be
+  equal bit for bit, and both must match the oracle.
+* Long-sequence chunking ("DeepSeek-V4 昇腾 NPU 推理部署实践", custom_params,
+  moe_chunk_max_len): rounds of at most `chunk` tokens give the same output
+  as one call, and each round's slots are the oracle's slots of that round.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as G
+import oracle
+from combine_get_dispatch_04_amd import api
+from combine_get_dispatch_04_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(name):
+    print(f"[case] {name}", flush=True)
+    sys.stdout.flush()
+
+
+def _native_ec(c):
+    x_d, ti_d = G.dev(c.x), G.dev(c.token_indices)
+    recv, off, ent, _ = G.ec_dispatch(x_d, ti_d)
+    out = G.ec_combine(recv, G.dev(c.weights), off, ent, c.T)
+    torch.cuda.synchronize()
+    return out
+
+
+def _emulated(tc):
+    x_d, idx_d = G.dev(tc.x), G.dev(tc.topk_idx)
+    L = G.layout(idx_d, tc.E)
+    recv, _, slot, _, _ = G.dispatch(x_d, idx_d, tc.E, L, False, tc.T * tc.K, sentinel=False)
+    out = G.combine(recv, slot, G.dev(tc.topk_weights))
+    torch.cuda.synchronize()
+    return out, slot
+
+
+@pytest.mark.parametrize("seed,T,H,E,C,hot,distinct", [
+    (1, 300, 264, 48, 30, 10, False),        # duplicates inside experts too
+    (2, 2000, 512, 64, 128, 64, True),       # tokens picked by all 64 experts
+    (3, 50, 64, 100, 8, 3, True),
+])
+def test_expert_choice_emulated_by_token_choice(seed, T, H, E, C, hot, distinct):
+    _announce(f"ec as tc T={T} E={E} C={C}")
+    c = W.random_expert_choice(seed, T, H, E, C, p_empty=0.1, hot=hot, distinct=distinct)
+    tc = W.as_token_choice(c)
+    native = G.host(_native_ec(c))
+    emu, slot = _emulated(tc)
+    emu = G.host(emu)
+    s_ref, _, _ = oracle.slots(tc.topk_idx, tc.E, False, tc.T * tc.K)
+    assert np.array_equal(G.host(slot), s_ref)
+    assert np.array_equal(native.view(np.uint16), emu.view(np.uint16))
+    ref = oracle.ec_combine(oracle.ec_dispatch(c.x, c.token_indices)[0], c.weights,
+                            c.token_indices, c.T)
+    G.assert_combine_close(emu, ref)
+
+
+def test_expert_choice_workload_emulated():
+    """The full expert-choice workload as [8192, 64] top-k (97 % padding)."""
+    _announce("ec workload as tc")
+    c = W.expert_choice()
+    tc = W.as_token_choice(c)
+    assert tc.K == 64
+    native = G.host(_native_ec(c))
+    emu, _ = _emulated(tc)
+    assert np.array_equal(native.view(np.uint16), G.host(emu).view(np.uint16))
+    toks = np.random.default_rng(5).choice(c.T, 256, replace=False)
+    ref = oracle.ec_combine(oracle.ec_dispatch(c.x, c.token_indices)[0], c.weights,
+                            c.token_indices, c.T, tokens=toks.astype(np.int32))
+    G.assert_combine_close(native[toks], ref)
+
+
+def _chunk_check(c, chunk, quant="bf16"):
+    x_d, idx_d, w_d = G.dev(c.x), G.dev(c.topk_idx), G.dev(c.topk_weights)
+    x_d = x_d.view(torch.bfloat16) if x_d.dtype != torch.bfloat16 else x_d
+    expert = None
+    if quant == "fp8_e4m3_g128":
+        def expert(recv, scales, L):
+            return (recv.float() * scales.repeat_interleave(128, dim=1)).to(torch.bfloat16)
+    out_c, rounds = api.dispatch_combine_chunked(x_d, idx_d, c.E, chunk=chunk, topk_weights=w_d,
+                                                 expert=expert, quant=quant, keep_rounds=True)
+    out_1 = api.dispatch_combine_chunked(x_d, idx_d, c.E, chunk=c.T, topk_weights=w_d,
+                                         expert=expert, quant=quant)
+    torch.cuda.synchronize()
+    assert len(rounds) == (c.T + chunk - 1) // chunk
+    for r, (L, h) in enumerate(rounds):
+        t0, t1 = r * chunk, min(c.T, (r + 1) * chunk)
+        s_ref, _, _ = oracle.slots(c.topk_idx[t0:t1], c.E, False, (t1 - t0) * c.K)
+        assert np.array_equal(G.host(h.slot), s_ref), r
+    a, b = G.host(out_c), G.host(out_1)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    return a
+
+
+@pytest.mark.parametrize("T,H,E,K,chunk", [(3000, 512, 32, 6, 700), (513, 264, 9, 3, 128),
+                                           (100, 64, 4, 2, 1)])
+def test_chunked_equals_unchunked(T, H, E, K, chunk):
+    _announce(f"chunked T={T} chunk={chunk}")
+    c = W.random_token_choice(T + chunk, T, H, E, K, p_pad=0.1, p_invalid=0.02, p_dup=0.1)
+    out = _chunk_check(c, chunk)
+    s_ref, _, _ = oracle.slots(c.topk_idx, c.E, False, T * K)
+    ref = oracle.combine(oracle.dispatch_bf16(c.x, s_ref, T * K), s_ref, c.topk_weights)
+    G.assert_combine_close(out, ref)
+
+
+def test_chunked_fp8_round_trip():
+    _announce("chunked fp8")
+    c = W.random_token_choice(9, 1500, 1024, 16, 4, p_pad=0.1)
+    _chunk_check(c, 400, quant="fp8_e4m3_g128")
+
+
+def test_chunked_prefill():
+    """The prefill workload in rounds of 1024 tokens."""
+    _announce("chunked prefill")
+    c = W.prefill()
+    out = _chunk_check(c, 1024)
+    toks = np.sort(np.random.default_rng(6).choice(c.T, 128, replace=False))
+    sub = c.topk_idx[toks]
+    s_ref, _, _ = oracle.slots(sub, c.E, False, toks.size * c.K)
+    ref = oracle.combine(oracle.dispatch_bf16(c.x[toks], s_ref, toks.size * c.K), s_ref,
+                         c.topk_weights[toks])
+    G.assert_combine_close(out[toks], ref)
