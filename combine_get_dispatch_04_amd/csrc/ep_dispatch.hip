@@ -97,7 +97,10 @@ __device__ __forceinline__ float block_max(float v)
     return m;
 }
 
-template <int PPT, int MODE>
+// One block per (token, row segment).  A thread handles PPT units of U
+// adjacent 16-byte pieces (U = 2 for the 8-bit codes when the row has an
+// even number of pieces, so that a lane stores 16 bytes of codes).
+template <int PPT, int MODE, int U>
 __global__ void __launch_bounds__(256)
 dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict__ topk_idx, int K,
                 int E, const int32_t *__restrict__ offsets, int padded, int cap_or_rows, int CT,
@@ -107,39 +110,46 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
                 int32_t *__restrict__ num_dropped)
 {
     constexpr bool QUANT = MODE != kQuantBf16;
+    static_assert(U == 1 || (U == 2 && QUANT), "pairs are for the quantised modes");
     const int t = blockIdx.x;
     const int tid = threadIdx.x, bd = blockDim.x;
     const int pieces = H >> 3;
+    const int units = pieces / U;
     const int seg0 = blockIdx.y * PPT * bd;
     if (t == 0 && blockIdx.y == 0)
         write_num_dropped(offsets, E, padded, cap_or_rows, num_dropped);
 
     const char *xrow = reinterpret_cast<const char *>(x) + (size_t)t * H * 2;
-    u32x4 v[PPT];
+    u32x4 v[PPT][U];
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-        int i = seg0 + tid + j * bd;
-        v[j] = i < pieces ? ld16(xrow + (size_t)i * 16) : u32x4{0u, 0u, 0u, 0u};
+        const int i = seg0 + tid + j * bd;
+#pragma unroll
+        for (int h = 0; h < U; ++h)
+            v[j][h] = i < units ? ld16(xrow + ((size_t)i * U + h) * 16) : u32x4{0u, 0u, 0u, 0u};
     }
 
-    // q: the piece's codes (8 bytes, or 4 for e2m1); sc: its group's scale
+    // q: the unit's codes (8U bytes, or 4U for e2m1); sc: its group's scale
     // (fp32 bits for the 128-channel groups, the e8m0 code for MX)
-    u32x2 q[QUANT ? PPT : 1];
+    u32x4 q[QUANT ? PPT : 1];
     uint32_t sc[QUANT ? PPT : 1];
     float tok_scale = 0.0f;
     if constexpr (QUANT) {
         // |x| of a (non-NaN) bf16 orders like the integer of its low 15 bits,
-        // so the piece's max comes from the packed bits; channels are decoded
+        // so the unit's max comes from the packed bits; channels are decoded
         // to fp32 only where they are encoded (fewer live registers)
         float amax[PPT];
 #pragma unroll
         for (int j = 0; j < PPT; ++j) {
-            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
             uint32_t m = 0u;
 #pragma unroll
-            for (int h = 0; h < 4; ++h)
-                m = max(m, max(w[h] & 0x7FFFu, (w[h] >> 16) & 0x7FFFu));
-            amax[j] = __uint_as_float(m << 16);      // out-of-row pieces are zeros
+            for (int h = 0; h < U; ++h) {
+                const uint32_t w[4] = {v[j][h].x, v[j][h].y, v[j][h].z, v[j][h].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    m = max(m, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+            }
+            amax[j] = __uint_as_float(m << 16);      // out-of-row units are zeros
         }
         if constexpr (is_token_mode(MODE)) {
             float a = 0.0f;
@@ -156,47 +166,58 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
         for (int j = 0; j < PPT; ++j) {
             float a = amax[j];
             if constexpr (MODE == kQuantFp8G128) {
-                // 16 lanes = one 128-channel group (pieces and blockDim are multiples of 16)
+                // 16/U lanes = one 128-channel group (units and blockDim are multiples of it)
 #pragma unroll
-                for (int o = 1; o < 16; o <<= 1)
+                for (int o = 1; o < 16 / U; o <<= 1)
                     a = fmaxf(a, __shfl_xor(a, o, kWave));
             } else if constexpr (is_mx_mode(MODE)) {
-                // 4 lanes = one 32-channel block (pieces and blockDim are multiples of 4)
-                a = fmaxf(a, __shfl_xor(a, 1, kWave));
-                a = fmaxf(a, __shfl_xor(a, 2, kWave));
-            }
-            const float f[8] = {bf16_lo(v[j].x), bf16_hi(v[j].x), bf16_lo(v[j].y),
-                                bf16_hi(v[j].y), bf16_lo(v[j].z), bf16_hi(v[j].z),
-                                bf16_lo(v[j].w), bf16_hi(v[j].w)};
-            uint32_t c[8];
-            if constexpr (is_mx_mode(MODE)) {
-                const int e = mx_shared_exponent(a, mx_emax(MODE));
-                // 2^-e as an fp32 pattern: e >= -127, and e <= 127 - emax for
-                // finite bf16 input, so 127 - e lies in [2, 254]: a normal number
-                const float m = __uint_as_float((uint32_t)(127 - e) << 23);
-                sc[j] = (uint32_t)(e + 127);
+                // 4/U lanes = one 32-channel block
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    c[u] = encode<MODE>(f[u] * m);
-            } else {
-                const float s = MODE == kQuantFp8G128 ? (a == 0.0f ? 0.0f : a / 448.0f) : tok_scale;
-                sc[j] = __float_as_uint(s);
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    c[u] = s == 0.0f ? 0u : encode<MODE>(f[u] / s);
+                for (int o = 1; o < 4 / U; o <<= 1)
+                    a = fmaxf(a, __shfl_xor(a, o, kWave));
             }
+            uint32_t c[8 * U];
+#pragma unroll
+            for (int h = 0; h < U; ++h) {
+                const float f[8] = {bf16_lo(v[j][h].x), bf16_hi(v[j][h].x), bf16_lo(v[j][h].y),
+                                    bf16_hi(v[j][h].y), bf16_lo(v[j][h].z), bf16_hi(v[j][h].z),
+                                    bf16_lo(v[j][h].w), bf16_hi(v[j][h].w)};
+                if constexpr (is_mx_mode(MODE)) {
+                    const int e = mx_shared_exponent(a, mx_emax(MODE));
+                    // 2^-e as an fp32 pattern: e >= -127, and e <= 127 - emax for
+                    // finite bf16 input, so 127 - e lies in [2, 254]: a normal number
+                    const float m = __uint_as_float((uint32_t)(127 - e) << 23);
+                    sc[j] = (uint32_t)(e + 127);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        c[8 * h + u] = encode<MODE>(f[u] * m);
+                } else {
+                    const float s = MODE == kQuantFp8G128 ? (a == 0.0f ? 0.0f : a / 448.0f)
+                                                          : tok_scale;
+                    sc[j] = __float_as_uint(s);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        c[8 * h + u] = s == 0.0f ? 0u : encode<MODE>(f[u] / s);
+                }
+            }
+            uint32_t wd[4] = {0u, 0u, 0u, 0u};
             if constexpr (MODE == kQuantMxE2M1) {
-                q[j].x = c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12) | (c[4] << 16) |
-                         (c[5] << 20) | (c[6] << 24) | (c[7] << 28);
-                q[j].y = 0u;
+#pragma unroll
+                for (int k = 0; k < U; ++k)
+                    wd[k] = c[8 * k] | (c[8 * k + 1] << 4) | (c[8 * k + 2] << 8) |
+                            (c[8 * k + 3] << 12) | (c[8 * k + 4] << 16) | (c[8 * k + 5] << 20) |
+                            (c[8 * k + 6] << 24) | (c[8 * k + 7] << 28);
             } else {
-                q[j].x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-                q[j].y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+#pragma unroll
+                for (int k = 0; k < 2 * U; ++k)
+                    wd[k] = c[4 * k] | (c[4 * k + 1] << 8) | (c[4 * k + 2] << 16) |
+                            (c[4 * k + 3] << 24);
             }
+            q[j] = u32x4{wd[0], wd[1], wd[2], wd[3]};
             // keep the packed words here: left to itself the compiler sinks
-            // the packing into the slot loop and keeps all 8 codes of every
-            // piece live (131 VGPRs instead of about 60 at 7 pieces)
-            asm volatile("" : "+v"(q[j].x), "+v"(q[j].y), "+v"(sc[j]));
+            // the packing into the slot loop and keeps every code of every
+            // unit live (131 VGPRs instead of about 60 at 7 pieces)
+            asm volatile("" : "+v"(q[j]), "+v"(sc[j]));
         }
     }
 
@@ -228,22 +249,29 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
         if constexpr (!QUANT) {
 #pragma unroll
             for (int j = 0; j < PPT; ++j)
-                row_st16(dst, (seg0 + tid + j * bd) * 16, v[j]);
+                row_st16(dst, (seg0 + tid + j * bd) * 16, v[j][0]);
         } else {
 #pragma unroll
             for (int j = 0; j < PPT; ++j) {
                 const int i = seg0 + tid + j * bd;
-                if constexpr (MODE == kQuantMxE2M1)
-                    row_st4(dst, i * 4, q[j].x);
-                else
-                    row_st8(dst, i * 8, q[j]);
+                if constexpr (MODE == kQuantMxE2M1) {
+                    if constexpr (U == 2)
+                        row_st8(dst, i * 8, u32x2{q[j].x, q[j].y});
+                    else
+                        row_st4(dst, i * 4, q[j].x);
+                } else {
+                    if constexpr (U == 2)
+                        row_st16(dst, i * 16, q[j]);
+                    else
+                        row_st8(dst, i * 8, u32x2{q[j].x, q[j].y});
+                }
                 if constexpr (MODE == kQuantFp8G128) {
-                    if ((tid & 15) == 0 && i < pieces)
-                        reinterpret_cast<float *>(recv_s)[(size_t)s * (H >> 7) + (i >> 4)] =
+                    if ((tid & (16 / U - 1)) == 0 && i < units)
+                        reinterpret_cast<float *>(recv_s)[(size_t)s * (H >> 7) + i / (16 / U)] =
                             __uint_as_float(sc[j]);
                 } else if constexpr (is_mx_mode(MODE)) {
-                    if ((tid & 3) == 0 && i < pieces)
-                        reinterpret_cast<uint8_t *>(recv_s)[(size_t)s * (H >> 5) + (i >> 2)] =
+                    if ((tid & (4 / U - 1)) == 0 && i < units)
+                        reinterpret_cast<uint8_t *>(recv_s)[(size_t)s * (H >> 5) + i / (4 / U)] =
                             (uint8_t)sc[j];
                 }
             }
@@ -284,7 +312,7 @@ RowShape row_shape(int pieces)
     return best;
 }
 
-template <int MODE>
+template <int MODE, int U>
 hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint16_t *x, int H,
                              const int32_t *topk_idx, const int32_t *offsets, int padded,
                              int cap_or_rows, void *recv_x, void *recv_s, int32_t *slot,
@@ -296,7 +324,7 @@ hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint
     dim3 grid(p.T, rs.nseg), block(rs.bd);
 #define EP_DISPATCH_CASE(N)                                                                      \
     case N:                                                                                      \
-        hipLaunchKernelGGL((dispatch_kernel<N, MODE>), grid, block, 0, s, x, H, topk_idx, p.K, \
+        hipLaunchKernelGGL((dispatch_kernel<N, MODE, U>), grid, block, 0, s, x, H, topk_idx, p.K, \
                            p.E, offsets, padded, cap_or_rows, p.CT, p.nchunk, hist, rank,       \
                            recv_x, recv_s, slot, recv_src, num_dropped);                         \
         break;
@@ -318,7 +346,10 @@ hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint
 
 }  // namespace
 
-bool dispatch_row_fits_one_block(int H) { return row_shape(H / 8).nseg == 1; }
+bool dispatch_row_fits_one_block(int H)
+{
+    return row_shape((H / 8) % 2 == 0 ? H / 16 : H / 8).nseg == 1;
+}
 
 hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const int32_t *topk_idx,
                            const int32_t *offsets, bool padded, int cap_or_rows, int quant,
@@ -332,19 +363,33 @@ hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const 
                            (int)padded, cap_or_rows, num_dropped);
         return hipGetLastError();
     }
-    RowShape rs = row_shape(H / 8);
-#define EP_MODE_CASE(M)                                                                          \
+    // 8-bit codes of rows with an even number of pieces go in pairs of pieces
+    // (16-byte stores; measured at prefill: fp8 per 128 channels 63 -> 56 us,
+    // MXFP8 71 -> 54 us); e2m1 stays at one piece (4-byte stores measured
+    // faster than 8-byte ones there: 31 vs 33 us)
+    const bool pairs = quant != kQuantBf16 && quant != kQuantMxE2M1 && (H / 8) % 2 == 0;
+    const RowShape rs = row_shape(pairs ? H / 16 : H / 8);
+#define EP_MODE_CASE(M, UU)                                                                      \
     case M:                                                                                      \
-        return launch_dispatch_t<M>(p, rs, x, H, topk_idx, offsets, padded, cap_or_rows, recv_x, \
-                                    recv_scales, slot, recv_src, num_dropped, hist, rank, s);
+        return launch_dispatch_t<M, UU>(p, rs, x, H, topk_idx, offsets, padded, cap_or_rows,     \
+                                        recv_x, recv_scales, slot, recv_src, num_dropped, hist,  \
+                                        rank, s);
+    if (!pairs) {
+        switch (quant) {
+            EP_MODE_CASE(kQuantBf16, 1)
+            EP_MODE_CASE(kQuantFp8Token, 1)
+            EP_MODE_CASE(kQuantInt8Token, 1)
+            EP_MODE_CASE(kQuantMxE2M1, 1)
+        default:
+            return hipErrorInvalidValue;   // the other modes have H % 32 == 0
+        }
+    }
     switch (quant) {
-        EP_MODE_CASE(kQuantBf16)
-        EP_MODE_CASE(kQuantFp8G128)
-        EP_MODE_CASE(kQuantFp8Token)
-        EP_MODE_CASE(kQuantInt8Token)
-        EP_MODE_CASE(kQuantMxE4M3)
-        EP_MODE_CASE(kQuantMxE5M2)
-        EP_MODE_CASE(kQuantMxE2M1)
+        EP_MODE_CASE(kQuantFp8G128, 2)
+        EP_MODE_CASE(kQuantFp8Token, 2)
+        EP_MODE_CASE(kQuantInt8Token, 2)
+        EP_MODE_CASE(kQuantMxE4M3, 2)
+        EP_MODE_CASE(kQuantMxE5M2, 2)
     default:
         return hipErrorInvalidValue;
     }

@@ -102,6 +102,17 @@ def test_quant_dispatch_parity(mode, T, H, E, K, lay, cap):
     _check(mode, c, padded, cap, *_run(mode, c, padded, cap))
 
 
+@pytest.mark.parametrize("mode", ["fp8_e4m3_token", "int8_token"])
+@pytest.mark.parametrize("T,H,E,K", [(77, 200, 6, 3),      # 25 pieces: one piece per thread
+                                     (5, 8, 2, 2),         # one piece per row
+                                     (40, 32768, 4, 2),    # 4096 pieces: the largest row
+                                     (9, 16376, 3, 2)])    # 2047 pieces, odd: one piece per thread
+def test_token_modes_row_shapes(mode, T, H, E, K):
+    _announce(f"token quant shapes {mode} T={T} H={H}")
+    c = _inputs(T + H, T, H, E, K)
+    _check(mode, c, False, T * K, *_run(mode, c, False, T * K))
+
+
 def _one_row(row_f32):
     x = W.bf16_bits(np.asarray(row_f32, np.float32)[None, :])
     idx = np.zeros((1, 1), np.int32)
