@@ -61,7 +61,10 @@ __device__ __forceinline__ void store_row(const float (&acc)[PPT][8], uint16_t *
     }
 }
 
-template <int PPT>
+// G source rows per round: their slots and weights are scalar loads, then
+// all G*PPT row pieces are requested before the first FMA.  A slot outside
+// [0, y_rows) gets a zero-length descriptor (no access) and no FMA.
+template <int PPT, int G>
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint16_t *__restrict__ y, int y_rows, int H,
                const int32_t *__restrict__ slot, const float *__restrict__ w, int K,
@@ -78,12 +81,49 @@ combine_kernel(const uint16_t *__restrict__ y, int y_rows, int H,
             acc[j][u] = 0.0f;
     const int32_t *srow = slot + (int64_t)t * K;
     const float *wrow = w ? w + (int64_t)t * K : nullptr;
-    for (int k = 0; k < K; ++k) {
-        const int s = srow[k];
-        if ((unsigned)s >= (unsigned)y_rows)
-            continue;
-        const float wk = wrow ? wrow[k] : 1.0f;
-        acc_row<PPT>(acc, reinterpret_cast<const char *>(y) + (size_t)s * H * 2, wk, seg0, pieces);
+    if constexpr (G == 1) {
+        for (int k = 0; k < K; ++k) {
+            const int s = srow[k];
+            if ((unsigned)s >= (unsigned)y_rows)
+                continue;
+            const float wk = wrow ? wrow[k] : 1.0f;
+            acc_row<PPT>(acc, reinterpret_cast<const char *>(y) + (size_t)s * H * 2, wk, seg0,
+                         pieces);
+        }
+    } else {
+        for (int k0 = 0; k0 < K; k0 += G) {
+            bool ok[G];
+            float wk[G];
+            u32x4 v[G][PPT];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int s = k0 + g < K ? srow[k0 + g] : -1;
+                ok[g] = (unsigned)s < (unsigned)y_rows;
+                const size_t row = ok[g] ? (size_t)s : 0;
+                wk[g] = ok[g] ? (wrow ? wrow[k0 + g] : 1.0f) : 0.0f;
+                const rsrc_t src = row_rsrc(reinterpret_cast<const char *>(y) + row * H * 2,
+                                            ok[g] ? pieces * 16 : 0);
+#pragma unroll
+                for (int j = 0; j < PPT; ++j)
+                    v[g][j] = row_ld16(src, (seg0 + threadIdx.x + j * blockDim.x) * 16);
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (!ok[g])
+                    continue;
+#pragma unroll
+                for (int j = 0; j < PPT; ++j) {
+                    acc[j][0] = fmaf(wk[g], bf16_lo(v[g][j].x), acc[j][0]);
+                    acc[j][1] = fmaf(wk[g], bf16_hi(v[g][j].x), acc[j][1]);
+                    acc[j][2] = fmaf(wk[g], bf16_lo(v[g][j].y), acc[j][2]);
+                    acc[j][3] = fmaf(wk[g], bf16_hi(v[g][j].y), acc[j][3]);
+                    acc[j][4] = fmaf(wk[g], bf16_lo(v[g][j].z), acc[j][4]);
+                    acc[j][5] = fmaf(wk[g], bf16_hi(v[g][j].z), acc[j][5]);
+                    acc[j][6] = fmaf(wk[g], bf16_lo(v[g][j].w), acc[j][6]);
+                    acc[j][7] = fmaf(wk[g], bf16_hi(v[g][j].w), acc[j][7]);
+                }
+            }
+        }
     }
     store_row<PPT>(acc, out, H, t, seg0, pieces);
 }
@@ -194,13 +234,28 @@ hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *s
 {
     if (T == 0)
         return hipSuccess;
-    RowShape rs = row_shape(H / 8, 8);
+    // Many source rows per token (K >= 12): at most 2 pieces per thread, so
+    // a row spreads over more blocks, and 4 rows requested per round.
+    // Measured on T=16384, K=16 (3.2 GB of rows): 683 -> 641 us; at K = 8
+    // (prefill) that shape was 4 us slower than 7 pieces per thread, one row
+    // per round.
+    const bool many = K >= 12;
+    RowShape rs = row_shape(H / 8, many ? 2 : 8);
     dim3 grid(T, rs.nseg), block(rs.bd);
 #define EP_COMBINE_CASE(N)                                                                       \
     case N:                                                                                      \
-        hipLaunchKernelGGL((combine_kernel<N>), grid, block, 0, s, y, y_rows, H, slot, w, K,  \
+        hipLaunchKernelGGL((combine_kernel<N, 1>), grid, block, 0, s, y, y_rows, H, slot, w, K, \
                            out);                                                         \
         break;
+    if (many) {
+        if (rs.ppt == 1)
+            hipLaunchKernelGGL((combine_kernel<1, 4>), grid, block, 0, s, y, y_rows, H, slot, w,
+                               K, out);
+        else
+            hipLaunchKernelGGL((combine_kernel<2, 4>), grid, block, 0, s, y, y_rows, H, slot, w,
+                               K, out);
+        return hipGetLastError();
+    }
     EP_PPT_SWITCH(rs.ppt, EP_COMBINE_CASE)
 #undef EP_COMBINE_CASE
     return hipGetLastError();

@@ -234,6 +234,8 @@ def test_fp8_every_e4m3_boundary():
 @pytest.mark.parametrize("T,H,E,K,weighted", [
     (1, 8, 1, 1, True), (50, 64, 6, 3, True), (513, 520, 16, 4, False),
     (300, 2056, 32, 6, True), (1000, 7168, 256, 8, True), (2000, 64, 100, 40, True),
+    # K >= 12: 2 pieces per thread, 4 rows per round (a ragged last round at 13)
+    (300, 7168, 64, 16, True), (257, 520, 20, 13, False), (100, 2056, 32, 12, True),
 ])
 def test_combine_parity(T, H, E, K, weighted):
     _announce(f"combine T={T} H={H} K={K} w={weighted}")
