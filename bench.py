@@ -16,7 +16,7 @@ ep_combine_expert_choice), large_padded.
 
 Also reported: per-operation times (HIP events on the stream the kernels run
 on, in a second pass after the timed region), a cold-cache pass (1 GiB of
-scratch written before each step, outside its events, so that neither L2 nor
+scratch read before each step, outside its events, so that neither L2 nor
 the 256 MB MALL holds the inputs), the roofline of the dominant
 kernel (algorithmic bytes per launch over its average duration, against
 8 TB/s), HBM traffic from the committed rocprofv3 counter summary when it was
@@ -323,7 +323,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--flush-mib", type=int, default=1024,
-                    help="cold pass: write this many MiB of scratch before each step, "
+                    help="cold pass: read this many MiB of scratch before each step, "
                          "outside the step's events (0 = no cold pass)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
@@ -353,7 +353,7 @@ def main():
         path = chunked_token_choice_path(c, N, torch, dev, sp, a.chunk)
     else:
         path = token_choice_path(c, N, torch, dev, sp)
-    flush = torch.empty(a.flush_mib << 20, dtype=torch.uint8, device=dev) if a.flush_mib else None
+    flush = torch.ones(a.flush_mib << 20, dtype=torch.uint8, device=dev) if a.flush_mib else None
     if a.copy_probe_mib:
         src = torch.ones(a.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -402,14 +402,15 @@ def main():
         launches[name] = launches.get(name, 0) + 1
     step_ev = np.array([e[0].elapsed_time(e[nops]) for e in ev]) * 1e3
 
-    # cold pass: before each step (outside its events) write flush_mib MiB of
-    # scratch, which evicts L2 and the 256 MB MALL
+    # cold pass: before each step (outside its events) read flush_mib MiB of
+    # scratch, which evicts L2 and the 256 MB MALL; a read leaves clean lines
+    # behind, so the step does not pay for writing back the flush
     cold = None
     if flush is not None:
         cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(a.steps)]
         for i in range(a.steps):
-            flush.fill_(i & 0xFF)
+            flush.sum(dtype=torch.int64)
             cev[i][0].record(stream)
             step()
             cev[i][1].record(stream)

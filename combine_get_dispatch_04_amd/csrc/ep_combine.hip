@@ -241,6 +241,8 @@ hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *s
     // per round.
     const bool many = K >= 12;
     RowShape rs = row_shape(H / 8, many ? 2 : 8);
+    if ((uint64_t)T * rs.bd > 0xFFFFFFFFull)      // work-items per grid dimension fit 32 bits
+        return hipErrorInvalidConfiguration;
     dim3 grid(T, rs.nseg), block(rs.bd);
 #define EP_COMBINE_CASE(N)                                                                       \
     case N:                                                                                      \
@@ -270,6 +272,8 @@ hipError_t launch_ec_combine(const uint16_t *y, const float *w, int E, int C, in
     // At most 2 pieces per thread (so a popular token's row is spread over
     // more blocks) and 16 row pieces in flight per thread.
     RowShape rs = row_shape(H / 8, 2);
+    if ((uint64_t)T * rs.bd > 0xFFFFFFFFull)
+        return hipErrorInvalidConfiguration;
     dim3 grid(T, rs.nseg), block(rs.bd);
     if (rs.ppt == 1)
         hipLaunchKernelGGL((ec_combine_kernel<1, 16>), grid, block, 0, s, y, w, E * C, H, tok_off,

@@ -321,6 +321,8 @@ hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint
 {
     if (is_token_mode(MODE) && rs.nseg != 1)      // the host checks H first
         return hipErrorInvalidValue;
+    if ((uint64_t)p.T * rs.bd > 0xFFFFFFFFull)    // work-items per grid dimension fit 32 bits
+        return hipErrorInvalidConfiguration;
     dim3 grid(p.T, rs.nseg), block(rs.bd);
 #define EP_DISPATCH_CASE(N)                                                                      \
     case N:                                                                                      \

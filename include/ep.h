@@ -26,7 +26,10 @@
  *     the end of the call's work.
  *   - Argument errors are found on the host before anything is enqueued and
  *     returned synchronously (EP_ERR_INVALID_ARG / EP_ERR_UNSUPPORTED /
- *     EP_ERR_WORKSPACE).  A failed launch returns EP_ERR_HIP.  Bad DATA
+ *     EP_ERR_WORKSPACE).  A failed launch returns EP_ERR_HIP, as does a
+ *     grid beyond the launch limit (about 16.7 million tokens or
+ *     expert-choice entries per call: T times up to 256 threads must fit in
+ *     32 bits), with nothing enqueued.  Bad DATA
  *     (an index out of range, a capacity overflow) never fails a call: it
  *     is counted in num_invalid / num_dropped and skipped, so every output
  *     stays defined.
