@@ -269,3 +269,28 @@ def test_prefill_scale_quant_contiguous(mode):
         assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32))
     else:
         assert np.array_equal(got_s, want_s)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_quant_edge_cases(mode):
+    """No tokens; a contiguous buffer of zero rows (every slot dropped); a
+    padded buffer with capacity 0; all padding."""
+    _announce(f"quant edges {mode}")
+    H = 64
+    q = MODES[mode]
+    idx0 = torch.empty((0, 3), dtype=torch.int32, device=G.DEV)
+    x0 = torch.empty((0, H), dtype=torch.bfloat16, device=G.DEV)
+    L = G.layout(idx0, 4)
+    _, _, _, _, nd = G.dispatch(x0, idx0, 4, L, False, 0, quant=q)
+    torch.cuda.synchronize()
+    assert int(G.host(nd)[0]) == 0
+    c = W.random_token_choice(3, 40, H, 4, 3, p_pad=0.1)
+    n_valid = int(((c.topk_idx >= 0) & (c.topk_idx < 4)).sum())
+    for padded, cap in ((False, 0), (True, 0)):
+        recv, sc, slot, src, nd = _run(mode, c, padded, cap)
+        assert (G.host(slot) == -1).all()
+        assert int(G.host(nd)[0]) == n_valid
+    c = W.random_token_choice(4, 30, H, 4, 2, p_pad=1.0)
+    recv, sc, slot, src, nd = _run(mode, c, True, 5)
+    assert (G.host(slot) == -1).all() and int(G.host(nd)[0]) == 0
+    assert (G.host(recv) == G.SENT8).all()
