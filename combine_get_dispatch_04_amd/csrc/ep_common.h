@@ -85,71 +85,59 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
-// ---------------------------------------------------------------- e4m3
-// fp32 -> OCP E4M3 code (bias 7, 3 mantissa bits, max finite 448, no inf),
-// round to nearest even.  Below 2^-6 the code is the subnormal count
-// m = round(|v| * 2^9) (exact scaling, hardware round-to-nearest-even; m = 8
-// is the code of 2^-6, so the ranges join).  From 2^-6 up, the fp32 pattern
-// is rounded to 3 mantissa bits in place (a carry moves into the exponent)
-// and the exponent is rebiased from 127 to 7.  |v| >= 464 saturates to 448.
-__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float v)
+// ---------------------------------------------------------------- fp8 / fp4
+// gfx950 converts fp32 to the OCP 8-bit formats (E4M3: bias 7, largest
+// finite 448, no infinity; E5M2: bias 15, largest finite 57344) and to E2M1
+// in hardware, rounding to nearest even and keeping the sign of zero.  On
+// every finite fp32 input these instructions give the same code as a
+// software round-to-nearest-even encoder, with two exceptions that callers
+// avoid: the plain fp8 conversions do not saturate (|v| >= 464 for E4M3,
+// >= 61440 for E5M2 give a NaN code), so an input that may reach them is
+// first bounded with med3 to the largest finite value, which rounds the same
+// way.  The E2M1 conversion saturates at 6 by itself.
+//
+// Four fp8 codes in one word, value i in byte i.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
 {
-    uint32_t u = __float_as_uint(v);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a >= 0x43E80000u) {                 // 464.0
-        code = 0x7Eu;
-    } else if (a < 0x3C800000u) {           // 2^-6
-        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-    } else {
-        uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-        code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);   // exponent - 127 + 7
-    }
-    return sign | code;
+    const uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0u, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+__device__ __forceinline__ uint32_t e5m2x4(float a, float b, float c, float d)
+{
+    const uint32_t w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0u, false);
+    return __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+}
+// Eight E2M1 codes of v[i] * 2^-E in one word, value 2i in the low nibble of
+// byte i and 2i+1 in the high nibble.  The scaled conversion reads only the
+// exponent field of its scale operand, so `e8m0` (= E + 127, 0..254) is
+// passed as that field: E = -127 gives the pattern of +0.0, which the
+// instruction takes as 2^-127.
+__device__ __forceinline__ uint32_t e2m1x8_scaled(const float (&v)[8], uint32_t e8m0)
+{
+    const float scale = __uint_as_float(e8m0 << 23);
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
 }
 
-// fp32 -> OCP E5M2 code (bias 15, 2 mantissa bits, largest finite 57344),
-// round to nearest even, saturating (no infinity is produced).  Below 2^-14
-// the code is the subnormal count round(|v| * 2^16); from 2^-14 up the
-// pattern is rounded to 2 mantissa bits in place and rebiased.  |v| >= 61440
-// (the midpoint above 57344) saturates.
-__device__ __forceinline__ uint32_t f32_to_e5m2_rne(float v)
+// ---------------------------------------------------------------- x / s
+// Division by a scale shared by many elements, with one reciprocal per
+// scale: r = RN(1/s), q0 = RN(x*r), the remainder x - s*q0 exactly (one
+// fma), q = RN(q0 + rem*r).  By Markstein's theorem (r correctly rounded,
+// q0 within one ulp) q is the correctly rounded quotient as long as the
+// remainder does not underflow.  With s >= 2^-64 that holds for every
+// quotient of magnitude 2^-11 or more; smaller quotients may be off in the
+// last place, but every E4M3 or int8 code of a quantity below 2^-11 is a
+// zero code either way, so the codes equal those of x / s.  The final copysign keeps
+// -0 (the fma sum of +0 and -0 is +0).  Checked for every pair of bf16
+// |x| <= amax with s = amax/448 and s = amax/127.
+constexpr float kFastDivMinScale = 0x1p-64f;
+__device__ __forceinline__ float div_by_scale(float x, float s, float r)
 {
-    uint32_t u = __float_as_uint(v);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a >= 0x47700000u) {                 // 61440.0
-        code = 0x7Bu;
-    } else if (a < 0x38800000u) {           // 2^-14
-        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 65536.0f);
-    } else {
-        uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);
-        code = (((r >> 23) - 112u) << 2) | ((r >> 21) & 3u);   // exponent - 127 + 15
-    }
-    return sign | code;
-}
-
-// fp32 -> OCP E2M1 4-bit code (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 = codes
-// 0..7, bit 3 the sign), round to nearest even, saturating at 6.  Below 1
-// the code is round(|v| * 2) (2 is the code of 1.0); from 1 up the pattern
-// is rounded to one mantissa bit in place and rebiased (bias 1).
-__device__ __forceinline__ uint32_t f32_to_e2m1_rne(float v)
-{
-    uint32_t u = __float_as_uint(v);
-    uint32_t sign = (u >> 28) & 0x8u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a >= 0x40C00000u) {                 // 6.0
-        code = 7u;
-    } else if (a < 0x3F800000u) {           // 1.0
-        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 2.0f);
-    } else {
-        uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
-        code = (((r >> 23) - 126u) << 1) | ((r >> 22) & 1u);   // exponent - 127 + 1
-    }
-    return sign | code;
+    const float q0 = x * r;
+    const float rem = fmaf(-q0, s, x);
+    return __builtin_copysignf(fmaf(rem, r, q0), x);
 }
 
 // fp32 -> int8 code (two's complement byte): round to nearest even, clamped

@@ -15,9 +15,11 @@
 // Quantisation groups map onto lanes: a 128-channel group is 16 consecutive
 // lanes and a 32-channel MX block 4 lanes, reduced with lane shuffles; a
 // per-token scale needs the whole row in one block (one row segment) and a
-// block reduction.  Scales are correctly rounded fp32 divisions, elements are
-// divided by them (also correctly rounded) or, for MX, multiplied by the
-// exact power of two 2^-E, then encoded with round-to-nearest-even.
+// block reduction.  Scales are correctly rounded fp32 divisions.  Elements
+// are divided by them with one reciprocal per scale and one correction step
+// (codes equal to those of the correctly rounded quotient) or, for MX,
+// multiplied by the exact power of two 2^-E, then encoded to nearest even by
+// gfx950's own conversion instructions.
 #include "ep_common.h"
 #include "ep_internal.h"
 
@@ -67,17 +69,11 @@ __host__ __device__ constexpr int64_t row_bytes(int m, int H)
     return m == kQuantBf16 ? 2 * (int64_t)H : (m == kQuantMxE2M1 ? H / 2 : (int64_t)H);
 }
 
-template <int MODE>
-__device__ __forceinline__ uint32_t encode(float v)
+// Four int8 codes in one word, value i in byte i.
+__device__ __forceinline__ uint32_t int8x4(float a, float b, float c, float d)
 {
-    if constexpr (MODE == kQuantInt8Token)
-        return f32_to_int8_rne(v);
-    else if constexpr (MODE == kQuantMxE5M2)
-        return f32_to_e5m2_rne(v);
-    else if constexpr (MODE == kQuantMxE2M1)
-        return f32_to_e2m1_rne(v);
-    else
-        return f32_to_e4m3_rne(v);
+    return f32_to_int8_rne(a) | (f32_to_int8_rne(b) << 8) | (f32_to_int8_rne(c) << 16) |
+           (f32_to_int8_rne(d) << 24);
 }
 
 // Max of v over the block (blockDim.x <= 256); every thread gets it.
@@ -176,42 +172,56 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
                 for (int o = 1; o < 4 / U; o <<= 1)
                     a = fmaxf(a, __shfl_xor(a, o, kWave));
             }
-            uint32_t c[8 * U];
+            uint32_t wd[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int h = 0; h < U; ++h) {
                 const float f[8] = {bf16_lo(v[j][h].x), bf16_hi(v[j][h].x), bf16_lo(v[j][h].y),
                                     bf16_hi(v[j][h].y), bf16_lo(v[j][h].z), bf16_hi(v[j][h].z),
                                     bf16_lo(v[j][h].w), bf16_hi(v[j][h].w)};
+                if constexpr (MODE == kQuantMxE2M1) {
+                    sc[j] = (uint32_t)(mx_shared_exponent(a, 2) + 127);
+                    wd[h] = e2m1x8_scaled(f, sc[j]);
+                    continue;
+                }
+                float g[8];
                 if constexpr (is_mx_mode(MODE)) {
                     const int e = mx_shared_exponent(a, mx_emax(MODE));
                     // 2^-e as an fp32 pattern: e >= -127, and e <= 127 - emax for
                     // finite bf16 input, so 127 - e lies in [2, 254]: a normal number
                     const float m = __uint_as_float((uint32_t)(127 - e) << 23);
+                    // |x| * 2^-e < 2^(emax+1): bound it to the largest finite code
+                    constexpr float top = MODE == kQuantMxE4M3 ? 448.0f : 57344.0f;
                     sc[j] = (uint32_t)(e + 127);
 #pragma unroll
                     for (int u = 0; u < 8; ++u)
-                        c[8 * h + u] = encode<MODE>(f[u] * m);
+                        g[u] = __builtin_amdgcn_fmed3f(f[u] * m, -top, top);
                 } else {
+                    // |x| <= a, so |x / s| <= 448 * (1 + 2^-23) < 464 (or 127.00002):
+                    // no bound needed before the e4m3 conversion
                     const float s = MODE == kQuantFp8G128 ? (a == 0.0f ? 0.0f : a / 448.0f)
                                                           : tok_scale;
                     sc[j] = __float_as_uint(s);
+                    if (s >= kFastDivMinScale) {
+                        const float r = 1.0f / s;
 #pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        c[8 * h + u] = s == 0.0f ? 0u : encode<MODE>(f[u] / s);
+                        for (int u = 0; u < 8; ++u)
+                            g[u] = div_by_scale(f[u], s, r);
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < 8; ++u)
+                            g[u] = s == 0.0f ? 0.0f : f[u] / s;    // a zero group codes as 0
+                    }
                 }
-            }
-            uint32_t wd[4] = {0u, 0u, 0u, 0u};
-            if constexpr (MODE == kQuantMxE2M1) {
-#pragma unroll
-                for (int k = 0; k < U; ++k)
-                    wd[k] = c[8 * k] | (c[8 * k + 1] << 4) | (c[8 * k + 2] << 8) |
-                            (c[8 * k + 3] << 12) | (c[8 * k + 4] << 16) | (c[8 * k + 5] << 20) |
-                            (c[8 * k + 6] << 24) | (c[8 * k + 7] << 28);
-            } else {
-#pragma unroll
-                for (int k = 0; k < 2 * U; ++k)
-                    wd[k] = c[4 * k] | (c[4 * k + 1] << 8) | (c[4 * k + 2] << 16) |
-                            (c[4 * k + 3] << 24);
+                if constexpr (MODE == kQuantInt8Token) {
+                    wd[2 * h] = int8x4(g[0], g[1], g[2], g[3]);
+                    wd[2 * h + 1] = int8x4(g[4], g[5], g[6], g[7]);
+                } else if constexpr (MODE == kQuantMxE5M2) {
+                    wd[2 * h] = e5m2x4(g[0], g[1], g[2], g[3]);
+                    wd[2 * h + 1] = e5m2x4(g[4], g[5], g[6], g[7]);
+                } else {
+                    wd[2 * h] = e4m3x4(g[0], g[1], g[2], g[3]);
+                    wd[2 * h + 1] = e4m3x4(g[4], g[5], g[6], g[7]);
+                }
             }
             q[j] = u32x4{wd[0], wd[1], wd[2], wd[3]};
             // keep the packed words here: left to itself the compiler sinks

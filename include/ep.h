@@ -150,7 +150,8 @@ ep_status_t ep_get_dispatch_layout(const int32_t *topk_idx, int T, int K, int E,
  *                           [rows, H/2] (e2m1: channel 2i in the low nibble
  *                           of byte i, 2i+1 in the high nibble).  Needs
  *                           H % 32 == 0.
- *   x            [T, H] bf16 in.
+ *   x            [T, H] bf16 in; finite for the quantised modes (an infinity
+ *                or NaN gives unspecified codes and scales in its group).
  *   topk_idx     [T, K] int32 in (the array given to ep_get_dispatch_layout).
  *   offsets      [E+1] int32 in, from ep_get_dispatch_layout.
  *   recv_x       [rows, row bytes] out (row bytes: 2H bf16, H for the 8-bit
