@@ -234,12 +234,14 @@ hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *s
 {
     if (T == 0)
         return hipSuccess;
-    // Many source rows per token (K >= 12): at most 2 pieces per thread, so
-    // a row spreads over more blocks, and 4 rows requested per round.
-    // Measured on T=16384, K=16 (3.2 GB of rows): 683 -> 641 us; at K = 8
-    // (prefill) that shape was 4 us slower than 7 pieces per thread, one row
+    // Many source rows per token (K >= 12), or few tokens (T < 1024, where
+    // the grid does not fill the chip and each row's round trips are the
+    // time): at most 2 pieces per thread, so a row spreads over more blocks,
+    // and 4 rows requested per round.  Measured on T=16384, K=16 (3.2 GB of
+    // rows): 683 -> 641 us; on T=128, K=8: 10.2 -> 9.2 us.  At K = 8 and
+    // T = 4096 that shape was 4 us slower than 7 pieces per thread, one row
     // per round.
-    const bool many = K >= 12;
+    const bool many = K >= 12 || T < 1024;
     RowShape rs = row_shape(H / 8, many ? 2 : 8);
     if ((uint64_t)T * rs.bd > 0xFFFFFFFFull)      // work-items per grid dimension fit 32 bits
         return hipErrorInvalidConfiguration;

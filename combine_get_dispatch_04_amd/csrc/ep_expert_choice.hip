@@ -566,28 +566,6 @@ int grid_for(int64_t n, int bd)
     return (int)g;
 }
 
-// LDS bytes one block may take on the current device (cached per device).
-int lds_limit()
-{
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
-        (void)hipGetLastError();
-        return 65536;
-    }
-    if (dev < 64 && cached[dev] > 0)
-        return cached[dev];
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-        v <= 0) {
-        (void)hipGetLastError();
-        v = 65536;
-    }
-    if (dev < 64)
-        cached[dev] = v;
-    return v;
-}
-
 #define EP_EC_PPT_SWITCH(PPT_VAR, CASE) \
     switch (PPT_VAR) {                  \
         CASE(1)                         \

@@ -64,4 +64,7 @@ hipError_t launch_ec_combine(const uint16_t *y, const float *w, int E, int C, in
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// LDS bytes one block may take on the current device (cached per device).
+int lds_limit();
+
 }  // namespace ep

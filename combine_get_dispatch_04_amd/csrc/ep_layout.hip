@@ -17,6 +17,8 @@
 // lanes x 8 entries), that block does this itself and there is one launch.
 // ep_dispatch later places entry (t,k) of expert e at
 // offsets[e] + chunk_base[t / CT][e] + local_rank[t, k].
+#include <algorithm>
+
 #include "ep_common.h"
 #include "ep_internal.h"
 
@@ -228,7 +230,7 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
 // are copied back coalesced.  Columns longer than a tile are done in
 // segments with the running sum kept in the column's thread.
 __global__ void __launch_bounds__(1024)
-layout_scan_kernel(int nchunk, int E, int R, int32_t *__restrict__ chunk_hist,
+layout_scan_kernel(int nchunk, int E, int R, int tile_ints, int32_t *__restrict__ chunk_hist,
                    const int32_t *__restrict__ rank_part, const int32_t *__restrict__ inval_part,
                    int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                    int32_t *__restrict__ tokens_per_rank, int32_t *__restrict__ num_invalid)
@@ -243,10 +245,10 @@ layout_scan_kernel(int nchunk, int E, int R, int32_t *__restrict__ chunk_hist,
         ++sh;
     const int seg = 1 << sh;
     const int ld = seg + 1;                       // odd row stride: no bank conflicts
-    int cpt = kScanTileInts / ld;                 // columns per tile
+    int cpt = tile_ints / ld;                     // columns per tile
     cpt = cpt < 1 ? 1 : (cpt > bd ? bd : cpt);
     int32_t *tile = sm;
-    int32_t *tot = sm + kScanTileInts;            // [E]
+    int32_t *tot = sm + tile_ints;                // [E]
     int *tmp = tot + E;                           // [32]
     for (int col0 = 0; col0 < ncol; col0 += cpt) {
         const int nc = min(cpt, ncol - col0);
@@ -403,12 +405,49 @@ hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunk), dim3(p.waves * kWave), p
             return err;
     }
     if (p.nchunk != 1) {
-        hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(1024),
-                           (size_t)(kScanTileInts + p.E + 32) * sizeof(int32_t), s, p.nchunk, p.E, p.R, hist,
-                           rpart, ipart, counts, offsets, tokens_per_rank, num_invalid);
+        // One tile holds every column when the device's LDS allows (gfx950:
+        // 160 KiB per block); otherwise the columns go in several tiles.
+        int seg = 1;
+        while (seg < p.nchunk && seg < kScanSeg)
+            seg <<= 1;
+        const long long want = (long long)(p.E + p.R + 1) * (seg + 1);
+        const long long room = (long long)lds_limit() / 4 - p.E - 32;
+        const int tile = (int)std::max<long long>(kScanTileInts, std::min(want, room));
+        const size_t dyn = (size_t)(tile + p.E + 32) * sizeof(int32_t);
+        if (dyn > 65536) {
+            hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(layout_scan_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)dyn);
+            if (err != hipSuccess)
+                return err;
+        }
+        hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(1024), dyn, s, p.nchunk, p.E, p.R,
+                           tile, hist, rpart, ipart, counts, offsets, tokens_per_rank,
+                           num_invalid);
         return hipGetLastError();
     }
     return hipSuccess;
+}
+
+int lds_limit()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return 65536;
+    }
+    if (dev < 64 && cached[dev] > 0)
+        return cached[dev];
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        v <= 0) {
+        (void)hipGetLastError();
+        v = 65536;
+    }
+    if (dev < 64)
+        cached[dev] = v;
+    return v;
 }
 
 }  // namespace ep

@@ -42,7 +42,8 @@ LAYOUT_CASES = [
     (700, 4, 1024, 128, 0.1, 0.01),      # R > 64 path
     (300, 3, 4096, 4, 0.0, 0.02),        # largest E
     (9000, 1, 2, 1, 0.5, 0.1),
-    (20000, 16, 384, 8, 0.15, 0.0),      # many chunks
+    (20000, 16, 384, 8, 0.15, 0.0),      # many chunks, every scan column in one LDS tile
+    (6000, 8, 4096, 16, 0.1, 0.01),      # many chunks and E = 4096: the scan takes several tiles
 ]
 
 
