@@ -353,7 +353,6 @@ def main():
         path = chunked_token_choice_path(c, N, torch, dev, sp, a.chunk)
     else:
         path = token_choice_path(c, N, torch, dev, sp)
-    flush = torch.ones(a.flush_mib << 20, dtype=torch.uint8, device=dev) if a.flush_mib else None
     if a.copy_probe_mib:
         src = torch.ones(a.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -404,9 +403,14 @@ def main():
 
     # cold pass: before each step (outside its events) read flush_mib MiB of
     # scratch, which evicts L2 and the 256 MB MALL; a read leaves clean lines
-    # behind, so the step does not pay for writing back the flush
+    # behind, so the step does not pay for writing back the flush.  The
+    # scratch is allocated and filled only now: written at start-up, it
+    # slowed the timed pass of the chunked workload by 41 us per step
+    # (204.5 -> 245.8 us) although that pass never touches it.
     cold = None
-    if flush is not None:
+    if a.flush_mib:
+        flush = torch.ones(a.flush_mib << 20, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
         cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(a.steps)]
         for i in range(a.steps):

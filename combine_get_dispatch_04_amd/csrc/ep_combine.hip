@@ -61,9 +61,9 @@ __device__ __forceinline__ void store_row(const float (&acc)[PPT][8], uint16_t *
     }
 }
 
-// G source rows per round: their slots and weights are scalar loads, then
-// all G*PPT row pieces are requested before the first FMA.  A slot outside
-// [0, y_rows) gets a zero-length descriptor (no access) and no FMA.
+// G == 1: one source row per round, its slot and weight scalar loads; slots
+// outside [0, y_rows) are skipped.  G > 1: G valid source rows per round,
+// all G*PPT row pieces requested before the first FMA.
 template <int PPT, int G>
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint16_t *__restrict__ y, int y_rows, int H,
@@ -91,36 +91,57 @@ combine_kernel(const uint16_t *__restrict__ y, int y_rows, int H,
                          pieces);
         }
     } else {
-        for (int k0 = 0; k0 < K; k0 += G) {
-            bool ok[G];
-            float wk[G];
-            u32x4 v[G][PPT];
+        // Each round takes the next G valid slots in ascending k, so padding
+        // and dropped slots cost no round trip: every wave loads 64 of the
+        // token's slots at once (one per lane; all waves of the block load
+        // the same ones), a ballot marks the valid ones, and each round reads
+        // its slots and weights out of that mask with readlane.
+        const int lane = threadIdx.x & (kWave - 1);
+        for (int k0 = 0; k0 < K; k0 += kWave) {
+            const int kk = k0 + lane;
+            const int sv = kk < K ? srow[kk] : -1;
+            const bool valid = (unsigned)sv < (unsigned)y_rows;
+            const float wv = valid ? (wrow ? wrow[kk] : 1.0f) : 0.0f;
+            uint64_t m = ballot(valid);
+            while (m) {
+                int sel[G];
+                float wk[G];
+                bool ok[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const int s = k0 + g < K ? srow[k0 + g] : -1;
-                ok[g] = (unsigned)s < (unsigned)y_rows;
-                const size_t row = ok[g] ? (size_t)s : 0;
-                wk[g] = ok[g] ? (wrow ? wrow[k0 + g] : 1.0f) : 0.0f;
-                const rsrc_t src = row_rsrc(reinterpret_cast<const char *>(y) + row * H * 2,
-                                            ok[g] ? pieces * 16 : 0);
+                for (int g = 0; g < G; ++g) {
+                    ok[g] = m != 0;
+                    const int b = ok[g] ? (int)__builtin_ctzll(m) : 0;
+                    m &= m - 1;
+                    sel[g] = ok[g] ? __builtin_amdgcn_readlane(sv, b) : 0;
+                    wk[g] = ok[g] ? __int_as_float(
+                                        __builtin_amdgcn_readlane(__float_as_int(wv), b))
+                                  : 0.0f;
+                }
+                u32x4 v[G][PPT];
 #pragma unroll
-                for (int j = 0; j < PPT; ++j)
-                    v[g][j] = row_ld16(src, (seg0 + threadIdx.x + j * blockDim.x) * 16);
-            }
+                for (int g = 0; g < G; ++g) {
+                    const rsrc_t src = row_rsrc(reinterpret_cast<const char *>(y) +
+                                                    (size_t)sel[g] * H * 2,
+                                                ok[g] ? pieces * 16 : 0);
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                if (!ok[g])
-                    continue;
+                    for (int j = 0; j < PPT; ++j)
+                        v[g][j] = row_ld16(src, (seg0 + threadIdx.x + j * blockDim.x) * 16);
+                }
 #pragma unroll
-                for (int j = 0; j < PPT; ++j) {
-                    acc[j][0] = fmaf(wk[g], bf16_lo(v[g][j].x), acc[j][0]);
-                    acc[j][1] = fmaf(wk[g], bf16_hi(v[g][j].x), acc[j][1]);
-                    acc[j][2] = fmaf(wk[g], bf16_lo(v[g][j].y), acc[j][2]);
-                    acc[j][3] = fmaf(wk[g], bf16_hi(v[g][j].y), acc[j][3]);
-                    acc[j][4] = fmaf(wk[g], bf16_lo(v[g][j].z), acc[j][4]);
-                    acc[j][5] = fmaf(wk[g], bf16_hi(v[g][j].z), acc[j][5]);
-                    acc[j][6] = fmaf(wk[g], bf16_lo(v[g][j].w), acc[j][6]);
-                    acc[j][7] = fmaf(wk[g], bf16_hi(v[g][j].w), acc[j][7]);
+                for (int g = 0; g < G; ++g) {
+                    if (!ok[g])
+                        continue;
+#pragma unroll
+                    for (int j = 0; j < PPT; ++j) {
+                        acc[j][0] = fmaf(wk[g], bf16_lo(v[g][j].x), acc[j][0]);
+                        acc[j][1] = fmaf(wk[g], bf16_hi(v[g][j].x), acc[j][1]);
+                        acc[j][2] = fmaf(wk[g], bf16_lo(v[g][j].y), acc[j][2]);
+                        acc[j][3] = fmaf(wk[g], bf16_hi(v[g][j].y), acc[j][3]);
+                        acc[j][4] = fmaf(wk[g], bf16_lo(v[g][j].z), acc[j][4]);
+                        acc[j][5] = fmaf(wk[g], bf16_hi(v[g][j].z), acc[j][5]);
+                        acc[j][6] = fmaf(wk[g], bf16_lo(v[g][j].w), acc[j][6]);
+                        acc[j][7] = fmaf(wk[g], bf16_hi(v[g][j].w), acc[j][7]);
+                    }
                 }
             }
         }
