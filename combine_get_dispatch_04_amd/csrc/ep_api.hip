@@ -1,4 +1,4 @@
-// ep_api.cpp -- the C ABI declared in include/ep.h: argument checks,
+// ep_api.hip -- the C ABI declared in include/ep.h: argument checks,
 // workspace sizing, and stream-ordered launches of the gfx950 kernels.
 // Every check happens before anything is enqueued, so a rejected call has
 // no effect.  Nothing here touches the GPU except the launches.
@@ -14,6 +14,7 @@ constexpr int kMaxExperts = 4096;   // the layout keeps per-expert counts in LDS
 constexpr int kMaxRanks = 1024;
 constexpr int kMaxTopk = 1024;      // a chunk of the layout holds at least one token's row
 constexpr int64_t kI32 = 2147483647LL;
+constexpr int kMaxHidden = 1 << 24; // row byte counts and offsets stay 32-bit in the kernels
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -116,6 +117,8 @@ ep_status_t ep_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx
     if (H < 8 || H % 8 != 0 || (quant == EP_QUANT_FP8_E4M3_G128 && H % 128 != 0) ||
         (mx && H % 32 != 0))
         return EP_ERR_INVALID_ARG;
+    if (H > kMaxHidden)
+        return EP_ERR_UNSUPPORTED;
     if (per_token && !ep::dispatch_row_fits_one_block(H))
         return EP_ERR_UNSUPPORTED;
     if (cap_or_max_rows < 0)
@@ -145,6 +148,8 @@ ep_status_t ep_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot
 {
     if (T < 0 || K < 1 || H < 8 || H % 8 != 0 || (int64_t)T * K > kI32 || y_rows < 0)
         return EP_ERR_INVALID_ARG;
+    if (H > kMaxHidden)
+        return EP_ERR_UNSUPPORTED;
     if (T > 0 && (!slot || !out || (y_rows > 0 && !y)))
         return EP_ERR_INVALID_ARG;
     if (!aligned(y, 16) || !aligned(out, 16) || !aligned(slot, 4) || !aligned(topk_weights, 4))
@@ -161,6 +166,8 @@ ep_status_t ep_dispatch_expert_choice(const uint16_t *x, int T, int H,
 {
     if (T < 0 || T >= kI32 || E < 1 || C < 1 || (int64_t)E * C > kI32 || H < 8 || H % 8 != 0)
         return EP_ERR_INVALID_ARG;
+    if (H > kMaxHidden)
+        return EP_ERR_UNSUPPORTED;
     if (!token_indices || !tok_off || !tok_ent || !num_invalid || !recv_x || (T > 0 && !x))
         return EP_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(token_indices, 4) ||
@@ -181,6 +188,8 @@ ep_status_t ep_combine_expert_choice(const uint16_t *y, const float *weights, in
 {
     if (T < 0 || T >= kI32 || E < 1 || C < 1 || (int64_t)E * C > kI32 || H < 8 || H % 8 != 0)
         return EP_ERR_INVALID_ARG;
+    if (H > kMaxHidden)
+        return EP_ERR_UNSUPPORTED;
     if (T > 0 && (!y || !weights || !tok_off || !tok_ent || !out))
         return EP_ERR_INVALID_ARG;
     if (!aligned(y, 16) || !aligned(out, 16) || !aligned(weights, 4) || !aligned(tok_off, 4) ||

@@ -34,7 +34,10 @@
  *     is counted in num_invalid / num_dropped and skipped, so every output
  *     stays defined.
  *   - Array base pointers must be 16-byte aligned; `ws` 256-byte aligned.
- *   - H % 8 == 0 (rows move in 16-byte pieces); T*K, E*C, rows*H < 2^31.
+ *   - H % 8 == 0 (rows move in 16-byte pieces) and H <= 2^24
+ *     (EP_ERR_UNSUPPORTED beyond: a row's byte count stays 32-bit); T*K,
+ *     E*C and receive row counts < 2^31.  Byte offsets into buffers are
+ *     64-bit, so buffers may exceed 4 GiB.
  *   - Results are deterministic: the same inputs give the same bytes.
  */
 #ifndef EP_H

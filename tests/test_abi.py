@@ -134,6 +134,7 @@ def _dispatch(**kw):
     (dict(num_dropped=None), N.EP_ERR_INVALID_ARG),
     (dict(K=0), N.EP_ERR_INVALID_ARG),
     (dict(E=9000), N.EP_ERR_UNSUPPORTED),
+    (dict(H=(1 << 24) + 8), N.EP_ERR_UNSUPPORTED),                   # row bytes stay 32-bit
     (dict(ws=None), N.EP_ERR_WORKSPACE),
     (dict(ws_bytes=100), N.EP_ERR_WORKSPACE),
 ])
@@ -152,6 +153,7 @@ def test_dispatch_rejects(kw, status):
     (dict(slot=None), N.EP_ERR_INVALID_ARG),
     (dict(out=B + 8), N.EP_ERR_INVALID_ARG),
     (dict(topk_weights=A + 1), N.EP_ERR_INVALID_ARG),
+    (dict(H=(1 << 24) + 8), N.EP_ERR_UNSUPPORTED),
 ])
 def test_combine_rejects(kw, status):
     args = dict(y=A, y_rows=32, H=256, slot=A, topk_weights=None, T=16, K=2, out=B, stream=None)
@@ -173,6 +175,7 @@ def test_combine_rejects(kw, status):
     (dict(ws=None), N.EP_ERR_WORKSPACE),
     (dict(ws_bytes=64), N.EP_ERR_WORKSPACE),
     (dict(E=1 << 16, C=1 << 16), N.EP_ERR_INVALID_ARG),
+    (dict(H=(1 << 24) + 8), N.EP_ERR_UNSUPPORTED),
 ])
 def test_ec_dispatch_rejects(kw, status):
     args = dict(x=A, T=16, H=64, token_indices=A, E=4, C=8, recv_x=B, tok_off=A, tok_ent=A,
@@ -187,6 +190,7 @@ def test_ec_dispatch_rejects(kw, status):
     (dict(weights=None), N.EP_ERR_INVALID_ARG),
     (dict(tok_off=None), N.EP_ERR_INVALID_ARG),
     (dict(out=B + 2), N.EP_ERR_INVALID_ARG),
+    (dict(H=(1 << 24) + 8), N.EP_ERR_UNSUPPORTED),
 ])
 def test_ec_combine_rejects(kw, status):
     args = dict(y=A, weights=A, E=4, C=8, H=64, tok_off=A, tok_ent=A, T=16, out=B, stream=None)
