@@ -304,7 +304,27 @@ def cpu_baseline(c, budget_s):
             break
     return {"value": reps * c.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} full pass(es) of the same workload ({what}; {c.T} tokens each), "
-                      f"{el:.1f} s on one host thread"}
+                      f"{el:.1f} s on one host thread",
+            "host_cpu": host_cpu_model(), "host_logical_cpus": os.cpu_count()}
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def inputs_sha256(c):
+    """SHA-256 of every input array, as handed to both the GPU path and the oracle."""
+    names = ("x", "token_indices", "weights") if hasattr(c, "token_indices") else \
+            ("x", "topk_idx", "topk_weights")
+    return {n: hashlib.sha256(np.ascontiguousarray(getattr(c, n)).tobytes()).hexdigest()
+            for n in names}
 
 
 def main():
@@ -467,6 +487,7 @@ def main():
                      "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": dom_us},
     }
     res["cold"] = cold
+    res["inputs_sha256"] = inputs_sha256(c)
     if a.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(c, a.cpu_budget)
     print(json.dumps(res), flush=True)
