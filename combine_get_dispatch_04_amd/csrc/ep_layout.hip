@@ -30,7 +30,8 @@ constexpr int kMaxWaves = 16;
 constexpr int kLdsInts = 16384;      // 64 KiB per block
 constexpr int kMaxRanks = 1024;
 constexpr int kEpl = 8;              // entries per lane of a wave's run (at most)
-constexpr long long kTargetChunks = 32;
+constexpr int kSingleEpl = 4;        // at most this many tiles per wave in the one-block form
+constexpr long long kTargetChunks = 64;
 constexpr int kScanSeg = 256;        // chunks per column segment in the scan
 constexpr int kScanTileInts = 16384 - 4096 - 32;
 
@@ -336,13 +337,17 @@ LayoutPlan make_layout_plan(int T, int K, int E, int R)
         return fit < 1 ? 1 : (fit > kMaxWaves ? kMaxWaves : fit);
     };
     // A wave's 64-entry tiles form a dependent chain (shared-memory count,
-    // ballots, count update), so runs are kept short and spread over many
-    // waves.  An input that fits one block (some epl <= kEpl) takes one
-    // block, which also finishes the scan: one launch.  Otherwise: the
-    // fewest entries per lane that keep about kTargetChunks chunks.
+    // ballots, count update), measured at about 0.85 us per tile, so runs
+    // are kept short and spread over many waves.  An input that one block
+    // covers with at most kSingleEpl tiles per wave takes one block, which
+    // also finishes the scan: one launch (8.3 us with 1 tile per wave, 10.2
+    // with 4; with 8 it was 13.7 us against 11.7 for chunks and a scan).
+    // Otherwise: the fewest entries per lane that keep about kTargetChunks
+    // chunks (64 rather than 32: the large workload's layout 27.6 -> 24.9 us
+    // with 4 tiles per wave instead of 8, and the same scan tile).
     const long long n = (long long)T * K;
     long long cap = 0;
-    for (int epl = 1; epl <= kEpl; epl *= 2) {
+    for (int epl = 1; epl <= kSingleEpl; epl *= 2) {
         const long long c = (long long)wmax_for(epl) * kWave * epl;
         if (n <= c) {
             p.epl = epl;
