@@ -39,12 +39,38 @@ PEAK_HBM_GBPS = 8000.0
 HEADLINE_METRIC = "dispatch+combine tokens/s & achieved HBM GB/s, T=4096 H=7168 E=256 top-8"
 
 
+def _code_only(text):
+    """C/C++ source without comments and with whitespace runs collapsed, so
+    that comment edits do not count as kernel changes."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif text[i] == '"':                       # string literal, kept whole
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
+    """SHA-256 over the library sources (csrc/), comments and whitespace
+    excluded: the counter summaries in profiles/ are valid while it holds."""
     d = os.path.join(ROOT, "combine_get_dispatch_04_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(d, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()
 
 

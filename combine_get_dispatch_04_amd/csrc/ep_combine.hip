@@ -8,11 +8,13 @@
 //     out[t] = bf16( sum over token t's entries j of w[j] * y[j] )
 //
 // One block per (token, row segment); each thread owns PPT 16-byte pieces
-// (8 channels each) and keeps 8*PPT fp32 accumulators.  For every source row
-// (block-uniform, so the row index and the weight are scalar loads) it loads
-// its pieces with non-temporal buffer loads (each y row is read once) and
-// accumulates with fp32 FMAs in ascending k / entry order, then rounds once
-// to bf16 (nearest even).  A token with no source row writes +0.
+// (8 channels each) and keeps 8*PPT fp32 accumulators.  Source rows are
+// block-uniform: their indices and weights live in scalar registers (scalar
+// loads, or one vector load of 64 slots and readlane in the batched form).
+// Each thread loads its pieces of a row with non-temporal buffer loads (each
+// y row is read once) and accumulates with fp32 FMAs in ascending k / entry
+// order, then rounds once to bf16 (nearest even).  A token with no source
+// row writes +0.
 #include "ep_common.h"
 #include "ep_internal.h"
 

@@ -13,13 +13,15 @@
 // addresses, so it runs on the scalar unit.
 //
 // Quantisation groups map onto lanes: a 128-channel group is 16 consecutive
-// lanes and a 32-channel MX block 4 lanes, reduced with lane shuffles; a
-// per-token scale needs the whole row in one block (one row segment) and a
-// block reduction.  Scales are correctly rounded fp32 divisions.  Elements
-// are divided by them with one reciprocal per scale and one correction step
-// (codes equal to those of the correctly rounded quotient) or, for MX,
-// multiplied by the exact power of two 2^-E, then encoded to nearest even by
-// gfx950's own conversion instructions.
+// lanes and a 32-channel MX block 4 lanes (8 and 2 when a lane holds two
+// pieces), reduced with lane shuffles; a per-token scale needs the whole row
+// in one block (one row segment) and a block reduction.  Scales are
+// correctly rounded fp32 divisions.  Elements are divided by them with one
+// reciprocal per scale and one correction step (codes equal to those of the
+// correctly rounded quotient) or, for MX, scaled by the exact power of two
+// 2^-E (a multiply for the fp8 widths, the conversion's scale operand for
+// e2m1), then encoded to nearest even by gfx950's own conversion
+// instructions.
 #include "ep_common.h"
 #include "ep_internal.h"
 
