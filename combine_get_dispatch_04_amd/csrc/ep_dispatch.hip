@@ -233,63 +233,77 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
         }
     }
 
+    // The token's slots, 64 at a time, one per lane: its experts and ranks
+    // are one coalesced load and the chunk bases one gather, instead of two
+    // dependent scalar loads per slot.  Every wave computes them (the waves
+    // of a block store the same slots); wave 0 of row segment 0 writes the
+    // handle.  The stores then take each slot with readlane.
     const int c = t / CT;
     const int32_t *trow = topk_idx + (int64_t)t * K;
     const int32_t *rrow = local_rank + (int64_t)t * K;
     const int64_t rb = row_bytes(MODE, H);
-    for (int k = 0; k < K; ++k) {
-        const int e = trow[k];
-        int s = -1;
-        if ((unsigned)e < (unsigned)E) {
-            const int r = chunk_base[(int64_t)e * nchunk + c] + rrow[k];
-            if (padded)
-                s = r < cap_or_rows ? e * cap_or_rows + r : -1;
-            else {
-                s = offsets[e] + r;
-                if (s >= cap_or_rows)
-                    s = -1;
-            }
-        }
-        if (blockIdx.y == 0 && tid == 0) {
-            slot_out[(int64_t)t * K + k] = s;
-            if (s >= 0 && recv_src)
-                recv_src[s] = t;
-        }
-        if (s < 0)
-            continue;
-        const rsrc_t dst = row_rsrc(reinterpret_cast<char *>(recv_x) + (size_t)s * rb, (int)rb);
-        if constexpr (!QUANT) {
-#pragma unroll
-            for (int j = 0; j < PPT; ++j)
-                row_st16(dst, (seg0 + tid + j * bd) * 16, v[j][0]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < PPT; ++j) {
-                const int i = seg0 + tid + j * bd;
-                if constexpr (MODE == kQuantMxE2M1) {
-                    if constexpr (U == 2)
-                        row_st8(dst, i * 8, u32x2{q[j].x, q[j].y});
-                    else
-                        row_st4(dst, i * 4, q[j].x);
-                } else {
-                    if constexpr (U == 2)
-                        row_st16(dst, i * 16, q[j]);
-                    else
-                        row_st8(dst, i * 8, u32x2{q[j].x, q[j].y});
-                }
-                if constexpr (MODE == kQuantFp8G128) {
-                    if ((tid & (16 / U - 1)) == 0 && i < units)
-                        reinterpret_cast<float *>(recv_s)[(size_t)s * (H >> 7) + i / (16 / U)] =
-                            __uint_as_float(sc[j]);
-                } else if constexpr (is_mx_mode(MODE)) {
-                    if ((tid & (4 / U - 1)) == 0 && i < units)
-                        reinterpret_cast<uint8_t *>(recv_s)[(size_t)s * (H >> 5) + i / (4 / U)] =
-                            (uint8_t)sc[j];
+    const int lane = tid & (kWave - 1);
+    const bool writer = blockIdx.y == 0 && tid < kWave;
+    for (int k0 = 0; k0 < K; k0 += kWave) {
+        const int k = k0 + lane;
+        int sl = -1;
+        if (k < K) {
+            const int e = trow[k];
+            if ((unsigned)e < (unsigned)E) {
+                const int r = chunk_base[(int64_t)e * nchunk + c] + rrow[k];
+                if (padded)
+                    sl = r < cap_or_rows ? e * cap_or_rows + r : -1;
+                else {
+                    sl = offsets[e] + r;
+                    if (sl >= cap_or_rows)
+                        sl = -1;
                 }
             }
-            if constexpr (is_token_mode(MODE)) {
-                if (tid == 0)
-                    reinterpret_cast<float *>(recv_s)[s] = tok_scale;
+            if (writer) {
+                slot_out[(int64_t)t * K + k] = sl;
+                if (sl >= 0 && recv_src)
+                    recv_src[sl] = t;
+            }
+        }
+        const int kn = K - k0 < kWave ? K - k0 : kWave;
+        for (int kk = 0; kk < kn; ++kk) {
+            const int s = __builtin_amdgcn_readlane(sl, kk);
+            if (s < 0)
+                continue;
+            const rsrc_t dst = row_rsrc(reinterpret_cast<char *>(recv_x) + (size_t)s * rb, (int)rb);
+            if constexpr (!QUANT) {
+#pragma unroll
+                for (int j = 0; j < PPT; ++j)
+                    row_st16(dst, (seg0 + tid + j * bd) * 16, v[j][0]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < PPT; ++j) {
+                    const int i = seg0 + tid + j * bd;
+                    if constexpr (MODE == kQuantMxE2M1) {
+                        if constexpr (U == 2)
+                            row_st8(dst, i * 8, u32x2{q[j].x, q[j].y});
+                        else
+                            row_st4(dst, i * 4, q[j].x);
+                    } else {
+                        if constexpr (U == 2)
+                            row_st16(dst, i * 16, q[j]);
+                        else
+                            row_st8(dst, i * 8, u32x2{q[j].x, q[j].y});
+                    }
+                    if constexpr (MODE == kQuantFp8G128) {
+                        if ((tid & (16 / U - 1)) == 0 && i < units)
+                            reinterpret_cast<float *>(recv_s)[(size_t)s * (H >> 7) + i / (16 / U)] =
+                                __uint_as_float(sc[j]);
+                    } else if constexpr (is_mx_mode(MODE)) {
+                        if ((tid & (4 / U - 1)) == 0 && i < units)
+                            reinterpret_cast<uint8_t *>(recv_s)[(size_t)s * (H >> 5) + i / (4 / U)] =
+                                (uint8_t)sc[j];
+                    }
+                }
+                if constexpr (is_token_mode(MODE)) {
+                    if (tid == 0)
+                        reinterpret_cast<float *>(recv_s)[s] = tok_scale;
+                }
             }
         }
     }
