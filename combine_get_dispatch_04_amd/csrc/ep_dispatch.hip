@@ -7,10 +7,10 @@
 //
 // Token-major: one block per (token, row segment).  The block reads its
 // piece of x[t] once into registers (16 bytes = 8 channels per thread per
-// piece), quantises it once, then for each of the token's K slots computes
-// the receive row from the layout tables and stores the piece there (buffer
-// stores bounded by the row).  The slot arithmetic reads only block-uniform
-// addresses, so it runs on the scalar unit.
+// piece), quantises it once, then computes the token's K receive rows from
+// the layout tables, one slot per lane, and stores the piece to each of
+// them (buffer stores bounded by the row), taking each slot into a scalar
+// register with readlane.
 //
 // Quantisation groups map onto lanes: a 128-channel group is 16 consecutive
 // lanes and a 32-channel MX block 4 lanes (8 and 2 when a lane holds two
