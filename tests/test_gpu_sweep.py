@@ -62,7 +62,7 @@ def _reference(mode, x, slot, rows):
     return oracle.dispatch_mx(x, slot, rows, mode)
 
 
-@pytest.mark.parametrize("i", range(105))
+@pytest.mark.parametrize("i", range(350))
 def test_token_choice_sweep(i):
     d = _draw(i)
     mode, T, H, E, K, padded, rng = d["mode"], d["T"], d["H"], d["E"], d["K"], d["padded"], d["rng"]
@@ -113,7 +113,7 @@ def test_token_choice_sweep(i):
         assert (s[~written] == G.SENT_E8M0).all()
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(72))
 def test_expert_choice_sweep(i):
     rng = np.random.default_rng(9000 + i)
     T = int(rng.integers(1, 4000))
