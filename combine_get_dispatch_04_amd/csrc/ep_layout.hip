@@ -27,12 +27,15 @@ namespace ep {
 namespace {
 
 constexpr int kMaxWaves = 16;
-constexpr int kLdsInts = 16384;      // 64 KiB per block
+constexpr int kLdsInts = 16384;      // chunk kernel: 64 KiB of LDS per block
 constexpr int kMaxRanks = 1024;
 constexpr int kEpl = 8;              // entries per lane of a wave's run (at most)
 constexpr int kSingleEpl = 4;        // at most this many tiles per wave in the one-block form
 constexpr long long kTargetChunks = 64;
 constexpr int kScanSeg = 256;        // chunks per column segment in the scan
+// The scan's smallest tile: what 64 KiB holds next to E = 4096 totals and
+// the 32-int scratch; the launch grows it to every column when the device's
+// LDS allows.
 constexpr int kScanTileInts = 16384 - 4096 - 32;
 
 // Offsets from per-expert totals held in shared memory: an exclusive scan
