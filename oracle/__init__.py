@@ -38,9 +38,14 @@ _I64 = ctypes.c_int64
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB)
+        # ORACLE_LIB names another build of oracle.c: the mutation test loads
+        # deliberately broken copies this way to show that the pins catch them
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        L = ctypes.CDLL(path)
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_f32.restype = ctypes.c_float
         L.oracle_bf16_from_f64.argtypes = [ctypes.c_double]
