@@ -95,6 +95,136 @@ __device__ __forceinline__ float block_max(float v)
     return m;
 }
 
+// Max |x| over one unit (U pieces of 8 bf16 channels).  |x| of a (non-NaN)
+// bf16 orders like the integer of its low 15 bits, so it comes from the
+// packed bits; a unit outside the row is zeros.
+template <int U>
+__device__ __forceinline__ float unit_amax(const u32x4 (&vj)[U])
+{
+    uint32_t m = 0u;
+#pragma unroll
+    for (int h = 0; h < U; ++h) {
+        const uint32_t w[4] = {vj[h].x, vj[h].y, vj[h].z, vj[h].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            m = max(m, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+    }
+    return __uint_as_float(m << 16);
+}
+
+// A unit's max reduced over the lanes of its scale group: 16/U lanes hold a
+// 128-channel group, 4/U lanes a 32-channel MX block (units and the lanes of
+// a wave are multiples of these).
+template <int MODE, int U>
+__device__ __forceinline__ float group_amax(float a)
+{
+    if constexpr (MODE == kQuantFp8G128) {
+#pragma unroll
+        for (int o = 1; o < 16 / U; o <<= 1)
+            a = fmaxf(a, __shfl_xor(a, o, kWave));
+    } else if constexpr (is_mx_mode(MODE)) {
+#pragma unroll
+        for (int o = 1; o < 4 / U; o <<= 1)
+            a = fmaxf(a, __shfl_xor(a, o, kWave));
+    }
+    return a;
+}
+
+// Lanes that share one scale (a power of two).
+template <int MODE, int U>
+__host__ __device__ constexpr int group_lanes()
+{
+    return MODE == kQuantFp8G128 ? 16 / U : (is_mx_mode(MODE) ? 4 / U : 1);
+}
+
+// Codes of one unit (8U bytes, or 4U for e2m1, in qj) and its group's
+// scale (fp32 bits for the 128-channel and per-token scales, the e8m0 code
+// for MX) from the group's max |x| `a`; per-token modes pass their scale.
+template <int MODE, int U>
+__device__ __forceinline__ void encode_unit(const u32x4 (&vj)[U], float a, float tok_scale,
+                                            u32x4 &qj, uint32_t &scj)
+{
+    uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int h = 0; h < U; ++h) {
+        const float f[8] = {bf16_lo(vj[h].x), bf16_hi(vj[h].x), bf16_lo(vj[h].y),
+                            bf16_hi(vj[h].y), bf16_lo(vj[h].z), bf16_hi(vj[h].z),
+                            bf16_lo(vj[h].w), bf16_hi(vj[h].w)};
+        if constexpr (MODE == kQuantMxE2M1) {
+            scj = (uint32_t)(mx_shared_exponent(a, 2) + 127);
+            wd[h] = e2m1x8_scaled(f, scj);
+            continue;
+        }
+        float g[8];
+        if constexpr (is_mx_mode(MODE)) {
+            const int e = mx_shared_exponent(a, mx_emax(MODE));
+            // 2^-e as an fp32 pattern: e >= -127, and e <= 127 - emax for
+            // finite bf16 input, so 127 - e lies in [2, 254]: a normal number
+            const float m = __uint_as_float((uint32_t)(127 - e) << 23);
+            // |x| * 2^-e < 2^(emax+1): bound it to the largest finite code
+            constexpr float top = MODE == kQuantMxE4M3 ? 448.0f : 57344.0f;
+            scj = (uint32_t)(e + 127);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                g[u] = __builtin_amdgcn_fmed3f(f[u] * m, -top, top);
+        } else {
+            // |x| <= a, so |x / s| <= 448 * (1 + 2^-23) < 464 (or 127.00002):
+            // no bound needed before the e4m3 conversion
+            const float s = MODE == kQuantFp8G128 ? (a == 0.0f ? 0.0f : a / 448.0f) : tok_scale;
+            scj = __float_as_uint(s);
+            if (s >= kFastDivMinScale) {
+                const float r = 1.0f / s;
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    g[u] = div_by_scale(f[u], s, r);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    g[u] = s == 0.0f ? 0.0f : f[u] / s;    // a zero group codes as 0
+            }
+        }
+        if constexpr (MODE == kQuantInt8Token) {
+            wd[2 * h] = int8x4(g[0], g[1], g[2], g[3]);
+            wd[2 * h + 1] = int8x4(g[4], g[5], g[6], g[7]);
+        } else if constexpr (MODE == kQuantMxE5M2) {
+            wd[2 * h] = e5m2x4(g[0], g[1], g[2], g[3]);
+            wd[2 * h + 1] = e5m2x4(g[4], g[5], g[6], g[7]);
+        } else {
+            wd[2 * h] = e4m3x4(g[0], g[1], g[2], g[3]);
+            wd[2 * h + 1] = e4m3x4(g[4], g[5], g[6], g[7]);
+        }
+    }
+    qj = u32x4{wd[0], wd[1], wd[2], wd[3]};
+}
+
+// Stores of one unit's codes and scale to receive row `s` (dst covers the
+// row's codes).  i = the unit's index in the row; `lead` lanes hold the
+// first unit of their scale group.
+template <int MODE, int U>
+__device__ __forceinline__ void store_unit(rsrc_t dst, int i, int units, int H, bool lead, int s,
+                                           u32x4 qj, uint32_t scj, void *recv_s)
+{
+    if constexpr (MODE == kQuantMxE2M1) {
+        if constexpr (U == 2)
+            row_st8(dst, i * 8, u32x2{qj.x, qj.y});
+        else
+            row_st4(dst, i * 4, qj.x);
+    } else {
+        if constexpr (U == 2)
+            row_st16(dst, i * 16, qj);
+        else
+            row_st8(dst, i * 8, u32x2{qj.x, qj.y});
+    }
+    if constexpr (MODE == kQuantFp8G128) {
+        if (lead && i < units)
+            reinterpret_cast<float *>(recv_s)[(size_t)s * (H >> 7) + i / (16 / U)] =
+                __uint_as_float(scj);
+    } else if constexpr (is_mx_mode(MODE)) {
+        if (lead && i < units)
+            reinterpret_cast<uint8_t *>(recv_s)[(size_t)s * (H >> 5) + i / (4 / U)] = (uint8_t)scj;
+    }
+}
+
 // One block per (token, row segment).  A thread handles PPT units of U
 // adjacent 16-byte pieces (U = 2 for the 8-bit codes when the row has an
 // even number of pieces, so that a lane stores 16 bytes of codes).
@@ -133,22 +263,12 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
     uint32_t sc[QUANT ? PPT : 1];
     float tok_scale = 0.0f;
     if constexpr (QUANT) {
-        // |x| of a (non-NaN) bf16 orders like the integer of its low 15 bits,
-        // so the unit's max comes from the packed bits; channels are decoded
-        // to fp32 only where they are encoded (fewer live registers)
+        // channels are decoded to fp32 only where they are encoded (fewer
+        // live registers)
         float amax[PPT];
 #pragma unroll
-        for (int j = 0; j < PPT; ++j) {
-            uint32_t m = 0u;
-#pragma unroll
-            for (int h = 0; h < U; ++h) {
-                const uint32_t w[4] = {v[j][h].x, v[j][h].y, v[j][h].z, v[j][h].w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    m = max(m, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
-            }
-            amax[j] = __uint_as_float(m << 16);      // out-of-row units are zeros
-        }
+        for (int j = 0; j < PPT; ++j)
+            amax[j] = unit_amax<U>(v[j]);
         if constexpr (is_token_mode(MODE)) {
             float a = 0.0f;
 #pragma unroll
@@ -162,70 +282,7 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
         }
 #pragma unroll
         for (int j = 0; j < PPT; ++j) {
-            float a = amax[j];
-            if constexpr (MODE == kQuantFp8G128) {
-                // 16/U lanes = one 128-channel group (units and blockDim are multiples of it)
-#pragma unroll
-                for (int o = 1; o < 16 / U; o <<= 1)
-                    a = fmaxf(a, __shfl_xor(a, o, kWave));
-            } else if constexpr (is_mx_mode(MODE)) {
-                // 4/U lanes = one 32-channel block
-#pragma unroll
-                for (int o = 1; o < 4 / U; o <<= 1)
-                    a = fmaxf(a, __shfl_xor(a, o, kWave));
-            }
-            uint32_t wd[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int h = 0; h < U; ++h) {
-                const float f[8] = {bf16_lo(v[j][h].x), bf16_hi(v[j][h].x), bf16_lo(v[j][h].y),
-                                    bf16_hi(v[j][h].y), bf16_lo(v[j][h].z), bf16_hi(v[j][h].z),
-                                    bf16_lo(v[j][h].w), bf16_hi(v[j][h].w)};
-                if constexpr (MODE == kQuantMxE2M1) {
-                    sc[j] = (uint32_t)(mx_shared_exponent(a, 2) + 127);
-                    wd[h] = e2m1x8_scaled(f, sc[j]);
-                    continue;
-                }
-                float g[8];
-                if constexpr (is_mx_mode(MODE)) {
-                    const int e = mx_shared_exponent(a, mx_emax(MODE));
-                    // 2^-e as an fp32 pattern: e >= -127, and e <= 127 - emax for
-                    // finite bf16 input, so 127 - e lies in [2, 254]: a normal number
-                    const float m = __uint_as_float((uint32_t)(127 - e) << 23);
-                    // |x| * 2^-e < 2^(emax+1): bound it to the largest finite code
-                    constexpr float top = MODE == kQuantMxE4M3 ? 448.0f : 57344.0f;
-                    sc[j] = (uint32_t)(e + 127);
-#pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        g[u] = __builtin_amdgcn_fmed3f(f[u] * m, -top, top);
-                } else {
-                    // |x| <= a, so |x / s| <= 448 * (1 + 2^-23) < 464 (or 127.00002):
-                    // no bound needed before the e4m3 conversion
-                    const float s = MODE == kQuantFp8G128 ? (a == 0.0f ? 0.0f : a / 448.0f)
-                                                          : tok_scale;
-                    sc[j] = __float_as_uint(s);
-                    if (s >= kFastDivMinScale) {
-                        const float r = 1.0f / s;
-#pragma unroll
-                        for (int u = 0; u < 8; ++u)
-                            g[u] = div_by_scale(f[u], s, r);
-                    } else {
-#pragma unroll
-                        for (int u = 0; u < 8; ++u)
-                            g[u] = s == 0.0f ? 0.0f : f[u] / s;    // a zero group codes as 0
-                    }
-                }
-                if constexpr (MODE == kQuantInt8Token) {
-                    wd[2 * h] = int8x4(g[0], g[1], g[2], g[3]);
-                    wd[2 * h + 1] = int8x4(g[4], g[5], g[6], g[7]);
-                } else if constexpr (MODE == kQuantMxE5M2) {
-                    wd[2 * h] = e5m2x4(g[0], g[1], g[2], g[3]);
-                    wd[2 * h + 1] = e5m2x4(g[4], g[5], g[6], g[7]);
-                } else {
-                    wd[2 * h] = e4m3x4(g[0], g[1], g[2], g[3]);
-                    wd[2 * h + 1] = e4m3x4(g[4], g[5], g[6], g[7]);
-                }
-            }
-            q[j] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+            encode_unit<MODE, U>(v[j], group_amax<MODE, U>(amax[j]), tok_scale, q[j], sc[j]);
             // keep the packed words here: left to itself the compiler sinks
             // the packing into the slot loop and keeps every code of every
             // unit live (131 VGPRs instead of about 60 at 7 pieces)
@@ -244,6 +301,7 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
     const int64_t rb = row_bytes(MODE, H);
     const int lane = tid & (kWave - 1);
     const bool writer = blockIdx.y == 0 && tid < kWave;
+    const bool lead = (tid & (group_lanes<MODE, U>() - 1)) == 0;
     for (int k0 = 0; k0 < K; k0 += kWave) {
         const int k = k0 + lane;
         int sl = -1;
@@ -277,29 +335,9 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
                     row_st16(dst, (seg0 + tid + j * bd) * 16, v[j][0]);
             } else {
 #pragma unroll
-                for (int j = 0; j < PPT; ++j) {
-                    const int i = seg0 + tid + j * bd;
-                    if constexpr (MODE == kQuantMxE2M1) {
-                        if constexpr (U == 2)
-                            row_st8(dst, i * 8, u32x2{q[j].x, q[j].y});
-                        else
-                            row_st4(dst, i * 4, q[j].x);
-                    } else {
-                        if constexpr (U == 2)
-                            row_st16(dst, i * 16, q[j]);
-                        else
-                            row_st8(dst, i * 8, u32x2{q[j].x, q[j].y});
-                    }
-                    if constexpr (MODE == kQuantFp8G128) {
-                        if ((tid & (16 / U - 1)) == 0 && i < units)
-                            reinterpret_cast<float *>(recv_s)[(size_t)s * (H >> 7) + i / (16 / U)] =
-                                __uint_as_float(sc[j]);
-                    } else if constexpr (is_mx_mode(MODE)) {
-                        if ((tid & (4 / U - 1)) == 0 && i < units)
-                            reinterpret_cast<uint8_t *>(recv_s)[(size_t)s * (H >> 5) + i / (4 / U)] =
-                                (uint8_t)sc[j];
-                    }
-                }
+                for (int j = 0; j < PPT; ++j)
+                    store_unit<MODE, U>(dst, seg0 + tid + j * bd, units, H, lead, s, q[j], sc[j],
+                                        recv_s);
                 if constexpr (is_token_mode(MODE)) {
                     if (tid == 0)
                         reinterpret_cast<float *>(recv_s)[s] = tok_scale;

@@ -404,10 +404,9 @@ hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *
     if ((long long)p.CT * p.K > (long long)p.waves * kWave * p.epl)
         return hipErrorInvalidValue;     // a chunk's entries must fit its waves
     if (p.nchunk > 0) {
-hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunk), dim3(p.waves * kWave), p.lds, s,
+        hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunk), dim3(p.waves * kWave), p.lds, s,
                            topk_idx, p.T, p.K, p.E, p.R, p.CT, p.nbits, p.epl, hist, rank, rpart,
                            ipart, is_token_in_rank, counts, offsets, tokens_per_rank, num_invalid);
-
         hipError_t err = hipGetLastError();
         if (err != hipSuccess)
             return err;
