@@ -20,8 +20,8 @@ import torch
 from . import _native as N
 
 
-def _stream() -> int:
-    return torch.cuda.current_stream().cuda_stream
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -39,6 +39,24 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int):
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(dev: torch.device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {dev}")
+
+
+def _out(out: Optional[torch.Tensor], shape, dev: torch.device) -> torch.Tensor:
+    """A caller's output tensor, checked before the kernel writes shape[0] rows
+    into it, or a new one."""
+    if out is None:
+        return torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must be {tuple(shape)}, got {tuple(out.shape)}")
+    _same_device(dev, out=out)
+    return out
 
 
 @dataclass
@@ -91,8 +109,10 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int
     tpr = torch.empty(R, dtype=torch.int32, device=dev)
     itr = torch.empty((T, R), dtype=torch.uint8, device=dev)
     ninv = torch.empty(1, dtype=torch.int32, device=dev)
-    N.ep_get_dispatch_layout(_ptr(topk_idx), T, K, E, R, _ptr(counts), _ptr(offsets), _ptr(tpr),
-                             _ptr(itr), _ptr(ninv), _ptr(ws), ws_bytes, _stream())
+    with torch.cuda.device(dev):
+        N.ep_get_dispatch_layout(_ptr(topk_idx), T, K, E, R, _ptr(counts), _ptr(offsets),
+                                 _ptr(tpr), _ptr(itr), _ptr(ninv), _ptr(ws), ws_bytes,
+                                 _stream(dev))
     return Layout(tpr, None, counts, itr, offsets, ninv, topk_idx, E, R, ws)
 
 
@@ -152,6 +172,7 @@ def dispatch(x: torch.Tensor, layout: Layout, *, quant: str = "bf16",
     else:
         raise ValueError(f"unknown receive layout {recv_layout!r}")
     dev = x.device
+    _same_device(dev, topk_idx=idx, workspace=layout.workspace)
     recv = torch.empty((rows, H // row_div), dtype=rdt, device=dev)
     scales = None
     if scale_shape is not None:
@@ -160,9 +181,10 @@ def dispatch(x: torch.Tensor, layout: Layout, *, quant: str = "bf16",
     slot = torch.empty((T, K), dtype=torch.int32, device=dev)
     src = torch.empty(rows, dtype=torch.int32, device=dev)
     nd = torch.empty(1, dtype=torch.int32, device=dev)
-    N.ep_dispatch(_ptr(x), T, H, _ptr(idx), K, E, _ptr(layout.offsets), lay, arg, q, _ptr(recv),
-                  _ptr(scales), _ptr(slot), _ptr(src), _ptr(nd), _ptr(layout.workspace),
-                  layout.workspace.numel(), _stream())
+    with torch.cuda.device(dev):
+        N.ep_dispatch(_ptr(x), T, H, _ptr(idx), K, E, _ptr(layout.offsets), lay, arg, q,
+                      _ptr(recv), _ptr(scales), _ptr(slot), _ptr(src), _ptr(nd),
+                      _ptr(layout.workspace), layout.workspace.numel(), _stream(dev))
     return recv, scales, Handle(slot, src, nd, rows, recv_layout, cap if lay else None)
 
 
@@ -176,10 +198,12 @@ def combine(y: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor
         _need(topk_weights, "topk_weights", torch.float32, 2)
         if tuple(topk_weights.shape) != (T, K):
             raise ValueError("topk_weights must be [T, K]")
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
-    N.ep_combine(_ptr(y), y.shape[0], H, _ptr(handle.slot), _ptr(topk_weights), T, K, _ptr(out),
-                 _stream())
+    dev = y.device
+    _same_device(dev, slot=handle.slot, topk_weights=topk_weights)
+    out = _out(out, (T, H), dev)
+    with torch.cuda.device(dev):
+        N.ep_combine(_ptr(y), y.shape[0], H, _ptr(handle.slot), _ptr(topk_weights), T, K,
+                     _ptr(out), _stream(dev))
     return out
 
 
@@ -228,6 +252,7 @@ def dispatch_expert_choice(x: torch.Tensor, token_indices: torch.Tensor, weights
     if tuple(weights.shape) != (E, C):
         raise ValueError("weights must be [E, C] like token_indices")
     dev = x.device
+    _same_device(dev, token_indices=token_indices, weights=weights)
     ws_bytes = N.ep_ec_workspace_bytes(T, E, C)
     if ws_bytes == 0:
         raise N.EpError("ep_ec_workspace_bytes", N.EP_ERR_INVALID_ARG)
@@ -236,8 +261,10 @@ def dispatch_expert_choice(x: torch.Tensor, token_indices: torch.Tensor, weights
     off = torch.empty(T + 1, dtype=torch.int32, device=dev)
     ent = torch.empty(E * C, dtype=torch.int32, device=dev)
     ninv = torch.empty(1, dtype=torch.int32, device=dev)
-    N.ep_dispatch_expert_choice(_ptr(x), T, H, _ptr(token_indices), E, C, _ptr(recv), _ptr(off),
-                                _ptr(ent), _ptr(ninv), _ptr(ws), ws_bytes, _stream())
+    with torch.cuda.device(dev):
+        N.ep_dispatch_expert_choice(_ptr(x), T, H, _ptr(token_indices), E, C, _ptr(recv),
+                                    _ptr(off), _ptr(ent), _ptr(ninv), _ptr(ws), ws_bytes,
+                                    _stream(dev))
     return recv, ExpertChoiceHandle(off, ent, weights, ninv, T)
 
 
@@ -246,8 +273,13 @@ def combine_expert_choice(y: torch.Tensor, handle: ExpertChoiceHandle,
     _need(y, "y", torch.bfloat16, 3)
     E, C, H = y.shape
     T = handle.num_tokens
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
-    N.ep_combine_expert_choice(_ptr(y), _ptr(handle.weights), E, C, H, _ptr(handle.tok_off),
-                               _ptr(handle.tok_ent), T, _ptr(out), _stream())
+    if tuple(handle.weights.shape) != (E, C):
+        raise ValueError(f"y is [{E}, {C}, H] but the handle's weights are "
+                         f"{tuple(handle.weights.shape)}")
+    dev = y.device
+    _same_device(dev, weights=handle.weights, tok_off=handle.tok_off, tok_ent=handle.tok_ent)
+    out = _out(out, (T, H), dev)
+    with torch.cuda.device(dev):
+        N.ep_combine_expert_choice(_ptr(y), _ptr(handle.weights), E, C, H, _ptr(handle.tok_off),
+                                   _ptr(handle.tok_ent), T, _ptr(out), _stream(dev))
     return out

@@ -1,0 +1,165 @@
+"""The torch front end (combine_get_dispatch_04_amd.api) against the oracle,
+and its argument checks.
+
+Each Buffer-style call of "DeepEP-Ascend" README, API Overview
+(get_dispatch_layout, dispatch in the contiguous and the low-latency padded
+form, combine) and the expert-centric pair of "[Feature Request] Support
+Expert-Choice Routing via Native Expert-Centric API", Solution 1, is run on
+seeded inputs and compared with the oracle: integers and codes bit for bit,
+combines within |gpu - oracle| <= 2^-7 |oracle| + 1e-3.  The checks of bad
+arguments raise before anything is launched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as G
+import oracle
+from combine_get_dispatch_04_amd import api
+from combine_get_dispatch_04_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _tc(seed, T=300, H=512, E=24, K=4):
+    c = W.random_token_choice(seed, T, H, E, K, p_pad=0.1, p_invalid=0.02, p_dup=0.1)
+    return c, G.dev(c.x), G.dev(c.topk_idx), G.dev(c.topk_weights)
+
+
+def _written(slot, rows):
+    m = np.zeros(rows, bool)
+    m[slot[slot >= 0]] = True
+    return m
+
+
+def test_layout_matches_oracle():
+    c, _, idx, _ = _tc(1, E=32)
+    L = api.get_dispatch_layout(idx, c.E, num_ranks=4)
+    torch.cuda.synchronize()
+    ref = oracle.layout(c.topk_idx, c.E, 4)
+    assert np.array_equal(G.host(L.num_tokens_per_expert), ref["counts"])
+    assert np.array_equal(G.host(L.offsets), ref["offsets"])
+    assert np.array_equal(G.host(L.num_tokens_per_rank), ref["tokens_per_rank"])
+    assert np.array_equal(G.host(L.is_token_in_rank), ref["is_token_in_rank"])
+    assert int(G.host(L.num_invalid)[0]) == ref["num_invalid"]
+    assert L.num_tokens_per_rdma_rank is None
+
+
+@pytest.mark.parametrize("recv_layout", ["contiguous", "padded"])
+def test_bf16_round_trip(recv_layout):
+    c, x, idx, w = _tc(2)
+    L = api.get_dispatch_layout(idx, c.E)
+    cap = 30 if recv_layout == "padded" else None
+    recv, scales, h = api.dispatch(x, L, recv_layout=recv_layout, cap=cap)
+    out = api.combine(recv, h, w)
+    torch.cuda.synchronize()
+    padded = recv_layout == "padded"
+    s_ref, src_ref, nd_ref = oracle.slots(c.topk_idx, c.E, padded, cap if padded else c.T * c.K)
+    assert scales is None and h.rows == recv.shape[0]
+    assert np.array_equal(G.host(h.slot), s_ref)
+    assert int(G.host(h.num_dropped)[0]) == nd_ref
+    rows = h.rows
+    m = _written(s_ref, rows)
+    y = oracle.dispatch_bf16(c.x, s_ref, rows)
+    assert np.array_equal(G.host(recv)[m], y[m])
+    assert np.array_equal(G.host(h.recv_src)[m], src_ref[m])
+    G.assert_combine_close(G.host(out), oracle.combine(y, s_ref, c.topk_weights))
+
+
+@pytest.mark.parametrize("quant,mode", [("fp8_e4m3_g128", None), ("int8", "int8_token"),
+                                        ("pertoken_fp8_e4m3", "fp8_e4m3_token"),
+                                        ("mx_fp8_e5m2", "mxfp8_e5m2"),
+                                        ("mx_fp4_e2m1", "mxfp4_e2m1")])
+def test_quantised_dispatch_and_aliases(quant, mode):
+    c, x, idx, _ = _tc(3)
+    L = api.get_dispatch_layout(idx, c.E)
+    recv, scales, h = api.dispatch(x, L, quant=quant)
+    torch.cuda.synchronize()
+    s_ref, _, _ = oracle.slots(c.topk_idx, c.E, False, c.T * c.K)
+    rows = c.T * c.K
+    if mode is None:
+        q, s = oracle.dispatch_fp8(c.x, s_ref, rows)
+    elif mode in oracle.TOKEN_FMT:
+        q, s = oracle.dispatch_token_quant(c.x, s_ref, rows, mode)
+    else:
+        q, s = oracle.dispatch_mx(c.x, s_ref, rows, mode)
+    m = _written(s_ref, rows)
+    got_q = recv.view(torch.uint8).cpu().numpy()
+    want = np.ascontiguousarray(q[m]).view(np.uint8).reshape(got_q[m].shape)
+    assert np.array_equal(got_q[m], want)
+    got_s = scales.cpu().numpy()
+    if got_s.dtype == np.float32:
+        assert np.array_equal(got_s[m].view(np.uint32), s[m].view(np.uint32))
+    else:
+        assert np.array_equal(got_s[m], s[m])
+
+
+def test_combine_into_given_out_and_unit_weights():
+    c, x, idx, _ = _tc(4)
+    L = api.get_dispatch_layout(idx, c.E)
+    recv, _, h = api.dispatch(x, L)
+    out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device="cuda")
+    r = api.combine(recv, h, None, out=out)
+    torch.cuda.synchronize()
+    assert r.data_ptr() == out.data_ptr()
+    s_ref, _, _ = oracle.slots(c.topk_idx, c.E, False, c.T * c.K)
+    y = oracle.dispatch_bf16(c.x, s_ref, c.T * c.K)
+    G.assert_combine_close(G.host(out), oracle.combine(y, s_ref, None))
+
+
+def test_expert_choice_round_trip():
+    c = W.random_expert_choice(5, 700, 256, 12, 40, p_empty=0.1, hot=6)
+    x, ti, w = G.dev(c.x), G.dev(c.token_indices), G.dev(c.weights)
+    recv, h = api.dispatch_expert_choice(x, ti, w)
+    out = api.combine_expert_choice(recv, h)
+    torch.cuda.synchronize()
+    r_ref, ninv = oracle.ec_dispatch(c.x, c.token_indices)
+    off, ent = oracle.ec_invert(c.token_indices, c.T)
+    assert int(G.host(h.num_invalid)[0]) == ninv
+    assert np.array_equal(G.host(h.tok_off), off)
+    n = int(off[-1])
+    assert np.array_equal(G.host(h.tok_ent)[:n], ent[:n])
+    filled = ((c.token_indices >= 0) & (c.token_indices < c.T)).reshape(-1)
+    got = G.host(recv).reshape(-1, c.H)
+    assert np.array_equal(got[filled], r_ref.reshape(-1, c.H)[filled])
+    G.assert_combine_close(G.host(out), oracle.ec_combine(r_ref, c.weights, c.token_indices, c.T))
+
+
+def test_bad_arguments_raise_before_launch():
+    c, x, idx, w = _tc(6, T=64, H=256, E=8, K=2)
+    L = api.get_dispatch_layout(idx, c.E)
+    recv, _, h = api.dispatch(x, L)
+    torch.cuda.synchronize()
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="out must be"):
+        api.combine(recv, h, w, out=torch.empty((c.T - 1, c.H), **bf))
+    with pytest.raises(ValueError, match="out must be"):
+        api.combine(recv, h, w, out=torch.empty((c.T, 2 * c.H), **bf))
+    with pytest.raises(ValueError, match="out must be"):
+        api.combine(recv, h, w, out=torch.empty((c.T, c.H), dtype=torch.float32,
+                                                device="cuda"))
+    with pytest.raises(ValueError, match="contiguous"):
+        api.combine(recv, h, w, out=torch.empty((c.H, c.T), **bf).t())
+    with pytest.raises(ValueError, match="topk_weights"):
+        api.combine(recv, h, w[:, :1].contiguous())
+    with pytest.raises(ValueError, match="GPU"):
+        api.combine(recv, h, w.cpu())
+    with pytest.raises(ValueError, match="unknown quant"):
+        api.dispatch(x, L, quant="fp16")
+    with pytest.raises(ValueError, match="cap"):
+        api.dispatch(x, L, recv_layout="padded")
+    with pytest.raises(ValueError, match="tokens"):
+        api.dispatch(x[:-1].contiguous(), L)
+    with pytest.raises(ValueError):                     # E beyond the supported 4096
+        api.get_dispatch_layout(idx, 5000)
+
+    ce = W.random_expert_choice(7, 50, 64, 4, 8, p_empty=0.0, hot=0)
+    xe, te, we = G.dev(ce.x), G.dev(ce.token_indices), G.dev(ce.weights)
+    with pytest.raises(ValueError, match="weights"):
+        api.dispatch_expert_choice(xe, te, we[:, :4].contiguous())
+    recv_e, he = api.dispatch_expert_choice(xe, te, we)
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError, match="out must be"):
+        api.combine_expert_choice(recv_e, he, out=torch.empty((ce.T + 1, ce.H), **bf))
+    with pytest.raises(ValueError, match="handle's weights"):
+        api.combine_expert_choice(recv_e[:2].contiguous(), he)
