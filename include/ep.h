@@ -50,20 +50,27 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status codes, receive layouts and quantisation modes are passed as
+ * int32_t, with the named values below.  (Not as the enum types: a C++
+ * function may not even read an enum parameter that holds a value outside
+ * its enumerators' range, and every value a caller passes is checked.) */
+typedef int32_t ep_status_t;
+enum {
     EP_OK = 0,
     EP_ERR_INVALID_ARG = 1,   /* a size, pointer or alignment is wrong */
     EP_ERR_UNSUPPORTED = 2,   /* a valid request outside what is built (e.g. E > 4096) */
     EP_ERR_WORKSPACE = 3,     /* ws is NULL, misaligned or smaller than required */
     EP_ERR_HIP = 4            /* the HIP runtime reported a launch error */
-} ep_status_t;
+};
 
-typedef enum {
+typedef int32_t ep_recv_layout_t;
+enum {
     EP_LAYOUT_CONTIGUOUS = 0, /* expert blocks back to back: expert e's rows start at offsets[e] */
     EP_LAYOUT_PADDED = 1      /* [E, cap] rows: expert e's rows start at e*cap (low-latency form) */
-} ep_recv_layout_t;
+};
 
-typedef enum {
+typedef int32_t ep_quant_t;
+enum {
     EP_QUANT_BF16 = 0,           /* rows copied as bf16 */
     EP_QUANT_FP8_E4M3_G128 = 1,  /* e4m3 codes + one fp32 scale per 128 channels */
     EP_QUANT_FP8_E4M3_TOKEN = 2, /* e4m3 codes + one fp32 scale per token ("pertoken_fp8_e4m3") */
@@ -71,7 +78,7 @@ typedef enum {
     EP_QUANT_MXFP8_E4M3 = 4,     /* e4m3 codes + one e8m0 scale per 32 channels ("mx_fp8_e4m3") */
     EP_QUANT_MXFP8_E5M2 = 5,     /* e5m2 codes + one e8m0 scale per 32 channels ("mx_fp8_e5m2") */
     EP_QUANT_MXFP4_E2M1 = 6      /* e2m1 codes, 2 per byte, + e8m0 per 32 ("mx_fp4_e2m1") */
-} ep_quant_t;
+};
 
 /* Human-readable name of a status code (static string). */
 const char *ep_status_string(ep_status_t status);
