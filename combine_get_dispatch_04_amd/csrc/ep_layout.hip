@@ -18,6 +18,7 @@
 // ep_dispatch later places entry (t,k) of expert e at
 // offsets[e] + chunk_base[t / CT][e] + local_rank[t, k].
 #include <algorithm>
+#include <atomic>
 
 #include "ep_common.h"
 #include "ep_internal.h"
@@ -438,14 +439,19 @@ hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *
 
 int lds_limit()
 {
-    static int cached[64] = {0};
+    // per-device cache; callers on several host threads may race to fill
+    // it, each with the same value
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
         (void)hipGetLastError();
         return 65536;
     }
-    if (dev < 64 && cached[dev] > 0)
-        return cached[dev];
+    if (dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
         v <= 0) {
@@ -453,7 +459,7 @@ int lds_limit()
         v = 65536;
     }
     if (dev < 64)
-        cached[dev] = v;
+        cached[dev].store(v, std::memory_order_relaxed);
     return v;
 }
 
