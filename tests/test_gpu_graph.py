@@ -49,9 +49,15 @@ def _same(g, e):
     return e["out"] is None or torch.equal(b(g["out"]), b(e["out"]))
 
 
-@pytest.mark.parametrize("quant", ["bf16", "fp8_e4m3_g128"])
-def test_token_choice_graph_replays(quant):
-    T, H, E, K = 777, 1024, 64, 6
+# (T, H, E, K, quant): one layout chunk; and 64 chunks over E = 384, whose
+# column scan takes more than 64 KiB of LDS (the launch path that sets the
+# kernel's shared-memory attribute)
+TC_GRAPH = [(777, 1024, 64, 6, "bf16"), (777, 1024, 64, 6, "fp8_e4m3_g128"),
+            (4096, 64, 384, 16, "bf16")]
+
+
+@pytest.mark.parametrize("T,H,E,K,quant", TC_GRAPH)
+def test_token_choice_graph_replays(T, H, E, K, quant):
     x_s, idx_s, w_s = _dev_tc(W.random_token_choice(50, T, H, E, K, p_pad=0.1, p_invalid=0.02))
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
@@ -76,9 +82,13 @@ def test_token_choice_graph_replays(quant):
         assert _same(graph_out, eager), r
 
 
-def test_expert_choice_graph_replays():
-    T, H, E, C = 1500, 512, 16, 64
+# (T, H, E, C): the inverse map inside the copy's launch; and in a launch
+# of its own with 104000 B of LDS
+EC_GRAPH = [(1500, 512, 16, 64), (13000, 8, 8, 1000)]
 
+
+@pytest.mark.parametrize("T,H,E,C", EC_GRAPH)
+def test_expert_choice_graph_replays(T, H, E, C):
     def inputs(seed):
         c = W.random_expert_choice(seed, T, H, E, C, p_empty=0.1, hot=5)
         return (torch.from_numpy(c.x.view(np.int16)).cuda().view(torch.bfloat16),
