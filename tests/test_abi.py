@@ -201,3 +201,49 @@ def test_ec_combine_rejects(kw, status):
 def test_binding_raises_on_error_status():
     with pytest.raises(N.EpError):
         N.ep_combine(A, 32, 12, A, None, 16, 2, B, None)
+
+
+C_USER = r"""
+#include "ep.h"
+#include <stdio.h>
+
+int main(void)
+{
+    ep_status_t st = EP_OK;
+    ep_recv_layout_t lay = EP_LAYOUT_PADDED;
+    ep_quant_t q = EP_QUANT_MXFP4_E2M1;
+    const int codes[] = {EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_WORKSPACE,
+                         EP_ERR_HIP, EP_LAYOUT_CONTIGUOUS, EP_LAYOUT_PADDED, EP_QUANT_BF16,
+                         EP_QUANT_FP8_E4M3_G128, EP_QUANT_FP8_E4M3_TOKEN, EP_QUANT_INT8_TOKEN,
+                         EP_QUANT_MXFP8_E4M3, EP_QUANT_MXFP8_E5M2, EP_QUANT_MXFP4_E2M1};
+    size_t b = ep_workspace_bytes(4096, 8, 256, 1) + ep_ec_workspace_bytes(8192, 64, 256);
+    st = ep_get_dispatch_layout(NULL, 4, 2, 8, 1, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL);
+    st |= ep_dispatch(NULL, 4, 64, NULL, 2, 8, NULL, lay, 8, q, NULL, NULL, NULL, NULL, NULL, NULL,
+                      0, NULL);
+    st |= ep_combine(NULL, 0, 64, NULL, NULL, 4, 2, NULL, NULL);
+    st |= ep_dispatch_expert_choice(NULL, 4, 64, NULL, 2, 2, NULL, NULL, NULL, NULL, NULL, 0, NULL);
+    st |= ep_combine_expert_choice(NULL, NULL, 2, 2, 64, NULL, NULL, 4, NULL, NULL);
+    printf("%d %s %zu %d\n", (int)st, ep_status_string(EP_ERR_WORKSPACE), b,
+           (int)(sizeof codes / sizeof codes[0]));
+    return st == 0;    /* every call above is rejected */
+}
+"""
+
+
+@pytest.mark.parametrize("std", ["c99", "c11"])
+def test_header_is_plain_c_and_links(tmp_path, std):
+    """A C program that includes ep.h under strict ISO C, uses every type,
+    constant and function, links against libep.so and runs: each call is an
+    argument error, reported synchronously without touching a device."""
+    src = tmp_path / "user.c"
+    src.write_text(C_USER)
+    exe = tmp_path / "user"
+    lib_dir = os.path.dirname(N.LIB_PATH)
+    subprocess.run(["gcc", f"-std={std}", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe),
+                    f"-L{lib_dir}", "-lep", f"-Wl,-rpath,{lib_dir}"],
+                   check=True, capture_output=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    first = r.stdout.split()
+    assert first[0] != "0" and "workspace" in r.stdout and first[-1] == "14"
