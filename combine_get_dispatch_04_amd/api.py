@@ -207,6 +207,43 @@ def combine(y: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor
     return out
 
 
+def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor,
+                         num_max_dispatch_tokens_per_rank: int, num_experts: int, *,
+                         quant: str = "fp8_e4m3_g128"):
+    """The decode-phase call of "DeepEP-Ascend" README, API Overview
+    (low_latency_dispatch(x, topk_idx, num_max_dispatch_tokens_per_rank,
+    num_experts)): layout, then dispatch into the capacity-padded buffer of
+    num_max_dispatch_tokens_per_rank rows per expert.  Quantised by default
+    (e4m3 with one fp32 scale per 128 channels); quant="bf16" turns it off.
+    -> (recv_x [E, cap, H or H/2], recv_scales [E, cap, ...] or None, Handle);
+    the shapes are views of the flat receive rows."""
+    E, cap = int(num_experts), int(num_max_dispatch_tokens_per_rank)
+    L = get_dispatch_layout(topk_idx, E)
+    recv, scales, h = dispatch(x, L, quant=quant, recv_layout="padded", cap=cap)
+    recv = recv.view(E, cap, *recv.shape[1:])
+    if scales is not None:
+        scales = scales.view(E, cap, *scales.shape[1:])
+    return recv, scales, h
+
+
+def low_latency_combine(y: torch.Tensor, topk_idx: torch.Tensor,
+                        topk_weights: Optional[torch.Tensor], handle: Handle,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The decode-phase combine of "DeepEP-Ascend" README, API Overview
+    (low_latency_combine(x, topk_idx, topk_weights, handle)): y holds the
+    experts' bf16 rows in the receive layout, [E, cap, H] or [E*cap, H];
+    out[t] = bf16(sum_k w[t,k] * y[slot[t,k]]) with fp32 sums.  topk_idx
+    must be the one the handle came from (its shape is checked; the slots in
+    the handle already encode it)."""
+    if y.dim() == 3:
+        _need(y, "y", torch.bfloat16, 3)
+        y = y.view(-1, y.shape[-1])
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    if tuple(topk_idx.shape) != tuple(handle.slot.shape):
+        raise ValueError("topk_idx does not match the handle")
+    return combine(y, handle, topk_weights, out=out)
+
+
 def dispatch_combine_chunked(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, *,
                              chunk: int, topk_weights: Optional[torch.Tensor] = None,
                              expert=None, quant: str = "bf16", num_ranks: int = 1,

@@ -163,3 +163,40 @@ def test_bad_arguments_raise_before_launch():
         api.combine_expert_choice(recv_e, he, out=torch.empty((ce.T + 1, ce.H), **bf))
     with pytest.raises(ValueError, match="handle's weights"):
         api.combine_expert_choice(recv_e[:2].contiguous(), he)
+
+
+@pytest.mark.parametrize("quant", ["fp8_e4m3_g128", "bf16"])
+def test_low_latency_pair(quant):
+    """low_latency_dispatch / low_latency_combine with the pages' arguments:
+    the decode shape class (T = 96 tokens, capacity 16 with overflow)."""
+    c = W.random_token_choice(8, 96, 512, 32, 6, p_pad=0.1, p_invalid=0.0, p_dup=0.05)
+    x, idx, w = G.dev(c.x), G.dev(c.topk_idx), G.dev(c.topk_weights)
+    cap = 16
+    recv, scales, h = api.low_latency_dispatch(x, idx, cap, c.E, quant=quant)
+    assert recv.shape[:2] == (c.E, cap)
+    s_ref, _, nd_ref = oracle.slots(c.topk_idx, c.E, True, cap)
+    rows = c.E * cap
+    torch.cuda.synchronize()
+    assert np.array_equal(G.host(h.slot), s_ref)
+    assert int(G.host(h.num_dropped)[0]) == nd_ref
+    m = _written(s_ref, rows)
+    if quant == "bf16":
+        y = oracle.dispatch_bf16(c.x, s_ref, rows)
+        assert np.array_equal(G.host(recv).reshape(rows, -1)[m], y[m])
+        y_d = recv
+    else:
+        q, s = oracle.dispatch_fp8(c.x, s_ref, rows)
+        assert scales.shape[:2] == (c.E, cap)
+        assert np.array_equal(recv.view(torch.uint8).reshape(rows, -1).cpu().numpy()[m], q[m])
+        assert np.array_equal(scales.reshape(rows, -1).cpu().numpy()[m].view(np.uint32),
+                              s[m].view(np.uint32))
+        # identity experts on the dequantised rows, built on the host
+        deq = (np.vectorize(oracle.e4m3_to_f32)(q).astype(np.float64)
+               * np.repeat(s.astype(np.float64), 128, axis=1))
+        y = oracle.bf16_from_f64(deq.reshape(-1)).reshape(rows, -1)
+        y_d = G.dev(y).view(c.E, cap, -1)
+    out = api.low_latency_combine(y_d, idx, w, h)
+    torch.cuda.synchronize()
+    G.assert_combine_close(G.host(out), oracle.combine(y, s_ref, c.topk_weights))
+    with pytest.raises(ValueError, match="handle"):
+        api.low_latency_combine(y_d, idx[:, :2].contiguous(), w, h)
