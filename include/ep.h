@@ -20,7 +20,8 @@
  *     N = number of valid (t,k) slots.
  *   - bf16 values travel as uint16_t bit patterns, fp8 e4m3 as uint8_t codes.
  *   - Every array pointer is DEVICE memory, row-major, owned by the caller;
- *     libep allocates nothing and keeps no state between calls.
+ *     libep allocates nothing and keeps no state between calls (beyond a
+ *     cache of each device's shared-memory size per block).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and runs asynchronously.  Outputs are valid once the stream reaches
  *     the end of the call's work.
