@@ -112,14 +112,11 @@ ep_status_t ep_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx
     const bool quantised = quant != EP_QUANT_BF16;
     const bool mx = quant == EP_QUANT_MXFP8_E4M3 || quant == EP_QUANT_MXFP8_E5M2 ||
                     quant == EP_QUANT_MXFP4_E2M1;
-    const bool per_token = quant == EP_QUANT_FP8_E4M3_TOKEN || quant == EP_QUANT_INT8_TOKEN;
     const bool padded = layout == EP_LAYOUT_PADDED;
     if (H < 8 || H % 8 != 0 || (quant == EP_QUANT_FP8_E4M3_G128 && H % 128 != 0) ||
         (mx && H % 32 != 0))
         return EP_ERR_INVALID_ARG;
     if (H > kMaxHidden)
-        return EP_ERR_UNSUPPORTED;
-    if (per_token && !ep::dispatch_row_fits_one_block(H))
         return EP_ERR_UNSUPPORTED;
     if (cap_or_max_rows < 0)
         return EP_ERR_INVALID_ARG;

@@ -14,8 +14,9 @@
 //
 // Quantisation groups map onto lanes: a 128-channel group is 16 consecutive
 // lanes and a 32-channel MX block 4 lanes (8 and 2 when a lane holds two
-// pieces), reduced with lane shuffles; a per-token scale needs the whole row
-// in one block (one row segment) and a block reduction.  Scales are
+// pieces), reduced with lane shuffles; a per-token scale is a block reduction
+// when the row fits one block, and otherwise comes from a pre-pass kernel
+// that takes each row's max into the workspace.  Scales are
 // correctly rounded fp32 divisions.  Elements are divided by them with one
 // reciprocal per scale and one correction step (codes equal to those of the
 // correctly rounded quotient) or, for MX, scaled by the exact power of two
@@ -235,7 +236,7 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
                 int nchunk, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ local_rank,
                 void *__restrict__ recv_x, void *__restrict__ recv_s,
                 int32_t *__restrict__ slot_out, int32_t *__restrict__ recv_src,
-                int32_t *__restrict__ num_dropped)
+                int32_t *__restrict__ num_dropped, const float *__restrict__ tok_amax)
 {
     constexpr bool QUANT = MODE != kQuantBf16;
     static_assert(U == 1 || (U == 2 && QUANT), "pairs are for the quantised modes");
@@ -271,10 +272,14 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
             amax[j] = unit_amax<U>(v[j]);
         if constexpr (is_token_mode(MODE)) {
             float a = 0.0f;
+            if (tok_amax) {
+                a = tok_amax[t];                      // a row over several blocks: taken before
+            } else {
 #pragma unroll
-            for (int j = 0; j < PPT; ++j)
-                a = fmaxf(a, amax[j]);
-            a = block_max(a);                         // the row is in this block: one segment
+                for (int j = 0; j < PPT; ++j)
+                    a = fmaxf(a, amax[j]);
+                a = block_max(a);                     // the row is in this block: one segment
+            }
 #pragma unroll
             for (int j = 0; j < PPT; ++j)
                 amax[j] = a;
@@ -339,12 +344,29 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
                     store_unit<MODE, U>(dst, seg0 + tid + j * bd, units, H, lead, s, q[j], sc[j],
                                         recv_s);
                 if constexpr (is_token_mode(MODE)) {
-                    if (tid == 0)
+                    if (tid == 0 && blockIdx.y == 0)
                         reinterpret_cast<float *>(recv_s)[s] = tok_scale;
                 }
             }
         }
     }
+}
+
+// Max |x| of each token's row (one block per token), for the per-token modes
+// when a row spans several dispatch blocks.  The same packed-bits max as the
+// dispatch itself, so the result is exact and equal to the one-block form.
+__global__ void __launch_bounds__(256)
+token_amax_kernel(const uint16_t *__restrict__ x, int H, float *__restrict__ tok_amax)
+{
+    const char *xrow = reinterpret_cast<const char *>(x) + (size_t)blockIdx.x * H * 2;
+    float a = 0.0f;
+    for (int i = threadIdx.x; i < (H >> 3); i += blockDim.x) {
+        const u32x4 v[1] = {ld16(xrow + (size_t)i * 16)};
+        a = fmaxf(a, unit_amax<1>(v));
+    }
+    a = block_max(a);
+    if (threadIdx.x == 0)
+        tok_amax[blockIdx.x] = a;
 }
 
 // Row pieces per thread and threads per block for a row of `pieces` 16-byte
@@ -381,10 +403,18 @@ hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint
                              const int32_t *topk_idx, const int32_t *offsets, int padded,
                              int cap_or_rows, void *recv_x, void *recv_s, int32_t *slot,
                              int32_t *recv_src, int32_t *num_dropped, const int32_t *hist,
-                             const int32_t *rank, hipStream_t s)
+                             const int32_t *rank, float *tamax_ws, hipStream_t s)
 {
-    if (is_token_mode(MODE) && rs.nseg != 1)      // the host checks H first
-        return hipErrorInvalidValue;
+    // A per-token scale needs the whole row's max; when the row spans several
+    // blocks it is taken first, into the workspace.
+    float *tok_amax = nullptr;
+    if (is_token_mode(MODE) && rs.nseg != 1) {
+        tok_amax = tamax_ws;
+        hipLaunchKernelGGL(token_amax_kernel, dim3(p.T), dim3(256), 0, s, x, H, tok_amax);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
     if ((uint64_t)p.T * rs.bd > 0xFFFFFFFFull)    // work-items per grid dimension fit 32 bits
         return hipErrorInvalidConfiguration;
     dim3 grid(p.T, rs.nseg), block(rs.bd);
@@ -392,7 +422,7 @@ hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint
     case N:                                                                                      \
         hipLaunchKernelGGL((dispatch_kernel<N, MODE, U>), grid, block, 0, s, x, H, topk_idx, p.K, \
                            p.E, offsets, padded, cap_or_rows, p.CT, p.nchunk, hist, rank,       \
-                           recv_x, recv_s, slot, recv_src, num_dropped);                         \
+                           recv_x, recv_s, slot, recv_src, num_dropped, tok_amax);               \
         break;
     switch (rs.ppt) {
         EP_DISPATCH_CASE(1)
@@ -412,11 +442,6 @@ hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint
 
 }  // namespace
 
-bool dispatch_row_fits_one_block(int H)
-{
-    return row_shape((H / 8) % 2 == 0 ? H / 16 : H / 8).nseg == 1;
-}
-
 hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const int32_t *topk_idx,
                            const int32_t *offsets, bool padded, int cap_or_rows, int quant,
                            void *recv_x, void *recv_scales, int32_t *slot, int32_t *recv_src,
@@ -424,6 +449,7 @@ hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const 
 {
     const int32_t *hist = reinterpret_cast<const int32_t *>(ws + p.off_hist);
     const int32_t *rank = reinterpret_cast<const int32_t *>(ws + p.off_rank);
+    float *tamax = reinterpret_cast<float *>(ws + p.off_tamax);
     if (p.T == 0) {
         hipLaunchKernelGGL(dropped_only_kernel, dim3(1), dim3(256), 0, s, offsets, p.E,
                            (int)padded, cap_or_rows, num_dropped);
@@ -447,7 +473,7 @@ hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const 
     case M:                                                                                      \
         return launch_dispatch_t<M, UU>(p, rs, x, H, topk_idx, offsets, padded, cap_or_rows,     \
                                         recv_x, recv_scales, slot, recv_src, num_dropped, hist,  \
-                                        rank, s);
+                                        rank, tamax, s);
     if (!pairs) {
         switch (quant) {
             EP_MODE_CASE(kQuantBf16, 1)

@@ -18,7 +18,9 @@ struct LayoutPlan {
     int nbits;     // bits needed for an expert id in [0, E)
     size_t lds;    // dynamic shared memory of the chunk kernel
     // workspace carve-up (byte offsets, 256-aligned)
-    size_t off_hist, off_rank, off_rpart, off_ipart, bytes;
+    // off_tamax: [T] fp32 row maxima for the per-token modes when a row spans
+    // several dispatch blocks
+    size_t off_hist, off_rank, off_rpart, off_ipart, off_tamax, bytes;
 };
 
 LayoutPlan make_layout_plan(int T, int K, int E, int R);
@@ -41,10 +43,6 @@ constexpr int kQuantInt8Token = 3;
 constexpr int kQuantMxE4M3 = 4;
 constexpr int kQuantMxE5M2 = 5;
 constexpr int kQuantMxE2M1 = 6;
-
-// True when a row of H channels is handled by one dispatch block (needed by
-// the per-token modes, whose scale is a reduction over the row).
-bool dispatch_row_fits_one_block(int H);
 
 hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const int32_t *topk_idx,
                            const int32_t *offsets, bool padded, int cap_or_rows, int quant,

@@ -390,6 +390,8 @@ LayoutPlan make_layout_plan(int T, int K, int E, int R)
     off = align256(off + (size_t)p.nchunk * R * 4);
     p.off_ipart = off;
     off = align256(off + (size_t)p.nchunk * 4);
+    p.off_tamax = off;
+    off = align256(off + (size_t)T * 4);
     p.bytes = off;
     return p;
 }

@@ -146,9 +146,9 @@ ep_status_t ep_get_dispatch_layout(const int32_t *topk_idx, int T, int K, int E,
  *                           (e4m3) or a / 127 (int8: q = x / s rounded to
  *                           nearest even, clamped to [-127, 127], stored as
  *                           two's complement bytes); recv_x uint8 [rows, H],
- *                           recv_scales fp32 [rows].  The row must fit one
- *                           block: H <= 32768 when H % 16 == 0, else
- *                           H <= 16384 (EP_ERR_UNSUPPORTED beyond).
+ *                           recv_scales fp32 [rows].  Any H: a row too long
+ *                           for one block gets its max from a first kernel
+ *                           (the workspace holds one float per token).
  *   EP_QUANT_MXFP8_E4M3, EP_QUANT_MXFP8_E5M2, EP_QUANT_MXFP4_E2M1: per token
  *                           and 32-channel block b, with a = max|x| over the
  *                           block: E = floor(log2(a)) - emax (emax = 8, 15,

@@ -119,9 +119,6 @@ def _dispatch(**kw):
     (dict(quant=5, recv_scales=None), N.EP_ERR_INVALID_ARG),
     (dict(quant=3, recv_scales=None), N.EP_ERR_INVALID_ARG),
     (dict(quant=2, recv_scales=A + 2), N.EP_ERR_INVALID_ARG),       # fp32 scales: 4-byte alignment
-    (dict(quant=3, H=16392, recv_scales=A), N.EP_ERR_UNSUPPORTED),   # per-token row beyond one block
-    (dict(quant=2, H=16392, recv_scales=A), N.EP_ERR_UNSUPPORTED),
-    (dict(quant=2, H=32784, recv_scales=A), N.EP_ERR_UNSUPPORTED),   # even pieces: up to 32768
     (dict(layout=5), N.EP_ERR_INVALID_ARG),
     (dict(cap_or_max_rows=-1), N.EP_ERR_INVALID_ARG),
     (dict(layout=1, E=4096, cap_or_max_rows=1 << 20), N.EP_ERR_INVALID_ARG),   # E*cap >= 2^31

@@ -49,6 +49,11 @@ def _round_trip(c, quant=None):
         q, s = oracle.dispatch_fp8(c.x, s_ref, rows)
         assert np.array_equal(G.host(recv)[kept], q[kept])
         assert np.array_equal(G.host(sc)[kept].view(np.uint32), s[kept].view(np.uint32))
+    elif quant in (N.EP_QUANT_FP8_E4M3_TOKEN, N.EP_QUANT_INT8_TOKEN):
+        mode = "fp8_e4m3_token" if quant == N.EP_QUANT_FP8_E4M3_TOKEN else "int8_token"
+        q, s = oracle.dispatch_token_quant(c.x, s_ref, rows, mode)
+        assert np.array_equal(G.host(recv)[kept], q[kept])
+        assert np.array_equal(G.host(sc)[kept].view(np.uint32), s[kept].view(np.uint32))
     else:
         mode = {N.EP_QUANT_MXFP8_E4M3: "mxfp8_e4m3", N.EP_QUANT_MXFP4_E2M1: "mxfp4_e2m1"}[quant]
         q, e = oracle.dispatch_mx(c.x, s_ref, rows, mode)
@@ -93,9 +98,11 @@ def test_largest_experts_and_ranks():
 
 
 @pytest.mark.parametrize("quant", [None, N.EP_QUANT_FP8_E4M3_G128, N.EP_QUANT_MXFP8_E4M3,
-                                   N.EP_QUANT_MXFP4_E2M1])
+                                   N.EP_QUANT_MXFP4_E2M1, N.EP_QUANT_FP8_E4M3_TOKEN,
+                                   N.EP_QUANT_INT8_TOKEN])
 def test_rows_of_a_million_channels(quant):
-    """H = 2^20: 131072 pieces per row, dozens of row segments per token."""
+    """H = 2^20: 131072 pieces per row, dozens of row segments per token (for
+    the per-token scales, the row max is taken by a kernel of its own first)."""
     _announce(f"H=2^20 quant={quant}")
     c = W.random_token_choice(34, 3, 1 << 20, 3, 2, p_pad=0.0, p_invalid=0.0, p_dup=0.0)
     _round_trip(c, quant)

@@ -105,8 +105,12 @@ def test_quant_dispatch_parity(mode, T, H, E, K, lay, cap):
 @pytest.mark.parametrize("mode", ["fp8_e4m3_token", "int8_token"])
 @pytest.mark.parametrize("T,H,E,K", [(77, 200, 6, 3),      # 25 pieces: one piece per thread
                                      (5, 8, 2, 2),         # one piece per row
-                                     (40, 32768, 4, 2),    # 4096 pieces: the largest row
-                                     (9, 16376, 3, 2)])    # 2047 pieces, odd: one piece per thread
+                                     (40, 32768, 4, 2),    # 4096 pieces: the largest one-block row
+                                     (9, 16376, 3, 2),     # 2047 pieces, odd: one piece per thread
+                                     # rows over several blocks: the row max comes first
+                                     (12, 32776, 3, 2),    # 4097 pieces, odd: 3 segments
+                                     (7, 40000, 3, 2),     # 5000 pieces: 2 segments, ragged
+                                     (10, 65536, 4, 3)])   # 8192 pieces: 2 full segments
 def test_token_modes_row_shapes(mode, T, H, E, K):
     _announce(f"token quant shapes {mode} T={T} H={H}")
     c = _inputs(T + H, T, H, E, K)
