@@ -9,9 +9,10 @@ synthetic tensors, resident in HBM before the timed region.  W untimed
 warm-up steps, then exactly K timed steps between two device
 synchronisations; one JSON line is printed.
 
-Other workloads (--workload): toy, decode (fp8 e4m3 with 128-channel scales
-into the padded [E, 128, H] buffer; combine reads bf16(q*s) rows made
-outside the timed region), expert_choice (ep_dispatch_expert_choice +
+Other workloads (--workload): toy, decode (ep_low_latency_dispatch, one
+launch, fp8 e4m3 with 128-channel scales into the padded [E, 128, H] buffer,
+then ep_combine over bf16(q*s) rows made outside the timed region; with
+--two-call the layout + dispatch pair), expert_choice (ep_dispatch_expert_choice +
 ep_combine_expert_choice), large_padded.
 
 Also reported: per-operation times (HIP events on the stream the kernels run
@@ -262,6 +263,61 @@ def token_choice_path(c, N, torch, dev, sp):
                 kern, alg, meta)
 
 
+def low_latency_path(c, N, torch, dev, sp):
+    """The decode step as its caller makes it: ep_low_latency_dispatch (one
+    launch: ranks, codes, scales and counts) into the padded [E, cap] rows,
+    then ep_combine."""
+    T, H, E, K, cap = c.T, c.H, c.E, c.K, c.cap
+    quant = c.quant
+    qname, row_bytes, scale_shape = QUANT_MODES[quant]
+    rows = E * cap
+    P = lambda t: t.data_ptr() if t is not None else None
+    x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    idx = torch.from_numpy(c.topk_idx).to(dev)
+    w = torch.from_numpy(c.topk_weights).to(dev)
+    n_valid = int(((c.topk_idx >= 0) & (c.topk_idx < E)).sum())
+    if quant == "bf16":
+        recv = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+        scales = None
+    else:
+        recv = torch.empty((rows, H // 2 if quant == "mxfp4_e2m1" else H), dtype=torch.uint8,
+                           device=dev)
+        ncol, sdt = scale_shape(H)
+        scales = torch.empty((rows, ncol) if ncol else (rows,), dtype=getattr(torch, sdt),
+                             device=dev)
+    slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+    src = torch.empty(rows, dtype=torch.int32, device=dev)
+    cnt = torch.empty(E, dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    qcode = getattr(N, qname)
+
+    def dispatch():
+        N.ep_low_latency_dispatch(P(x), T, H, P(idx), K, E, cap, qcode, P(recv), P(scales),
+                                  P(slot), P(src), P(cnt), P(nd), P(ninv), sp)
+
+    if quant != "bf16":
+        # identity expert on the dequantised rows, built once outside the timed region
+        dispatch()
+        torch.cuda.synchronize()
+        y = dequantise(torch, recv, scales, quant, H)
+        torch.cuda.synchronize()
+    else:
+        y = recv
+
+    def combine():
+        N.ep_combine(P(y), rows, H, P(slot), P(w), T, K, P(out), sp)
+
+    alg = {"dispatch": T * H * 2 + n_valid * row_bytes(H) + 2 * T * K * 4 + E * 4,
+           "combine": n_valid * H * 2 + T * H * 2 + 2 * T * K * 4}
+    kern = {"dispatch": "dispatch_kernel", "combine": "combine_kernel"}
+    meta = {"T": T, "H": H, "E": E, "top_k": K, "recv_layout": "padded", "quant": quant,
+            "cap": cap, "combine": "weighted", "valid_slots": n_valid,
+            "dispatch": "ep_low_latency_dispatch (one launch)"}
+    return Path(c.name, T, [("dispatch", dispatch), ("combine", combine)], kern, alg, meta)
+
+
 def expert_choice_path(c, N, torch, dev, sp):
     T, H, E, C = c.T, c.H, c.E, c.C
     P = lambda t: t.data_ptr()
@@ -366,6 +422,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=0,
                     help="run a token-choice step in rounds of at most this many tokens "
                          "(0 = one round)")
+    ap.add_argument("--two-call", action="store_true",
+                    help="decode: ep_get_dispatch_layout + ep_dispatch (padded) instead of "
+                         "the one-launch ep_low_latency_dispatch")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--flush-mib", type=int, default=1024,
@@ -397,6 +456,8 @@ def main():
         path = expert_choice_path(c, N, torch, dev, sp)
     elif a.chunk > 0:
         path = chunked_token_choice_path(c, N, torch, dev, sp, a.chunk)
+    elif a.workload == "decode" and not a.two_call:
+        path = low_latency_path(c, N, torch, dev, sp)
     else:
         path = token_choice_path(c, N, torch, dev, sp)
     if a.copy_probe_mib:

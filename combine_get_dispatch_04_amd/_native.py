@@ -28,6 +28,8 @@ SIGNATURES = {
     "ep_ec_workspace_bytes": (_SZ, [_I, _I, _I]),
     "ep_get_dispatch_layout": (_ST, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "ep_dispatch": (_ST, [_P, _I, _I, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "ep_low_latency_dispatch": (_ST, [_P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                                      _P, _P]),
     "ep_combine": (_ST, [_P, _I, _I, _P, _P, _I, _I, _P, _P]),
     "ep_dispatch_expert_choice": (_ST, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "ep_combine_expert_choice": (_ST, [_P, _P, _I, _I, _I, _P, _P, _I, _P, _P]),
@@ -89,6 +91,14 @@ def ep_dispatch(x, T, H, topk_idx, K, E, offsets, layout, cap_or_max_rows, quant
     st = lib().ep_dispatch(x, T, H, topk_idx, K, E, offsets, layout, cap_or_max_rows, quant,
                            recv_x, recv_scales, slot, recv_src, num_dropped, ws, ws_bytes, stream)
     return _check("ep_dispatch", st) if check else st
+
+
+def ep_low_latency_dispatch(x, T, H, topk_idx, K, E, cap, quant, recv_x, recv_scales, slot,
+                            recv_src, recv_count, num_dropped, num_invalid, stream, check=True):
+    st = lib().ep_low_latency_dispatch(x, T, H, topk_idx, K, E, cap, quant, recv_x, recv_scales,
+                                       slot, recv_src, recv_count, num_dropped, num_invalid,
+                                       stream)
+    return _check("ep_low_latency_dispatch", st) if check else st
 
 
 def ep_combine(y, y_rows, H, slot, topk_weights, T, K, out, stream, check=True):

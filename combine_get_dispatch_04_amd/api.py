@@ -84,6 +84,8 @@ class Handle:
     rows: int
     recv_layout: str
     cap: Optional[int]
+    recv_count: Optional[torch.Tensor] = None  # [E] int32, rows each expert holds (low latency)
+    num_invalid: Optional[torch.Tensor] = None  # [1] int32 (low latency)
 
 
 @dataclass
@@ -212,18 +214,50 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor,
                          quant: str = "fp8_e4m3_g128"):
     """The decode-phase call of "DeepEP-Ascend" README, API Overview
     (low_latency_dispatch(x, topk_idx, num_max_dispatch_tokens_per_rank,
-    num_experts)): layout, then dispatch into the capacity-padded buffer of
-    num_max_dispatch_tokens_per_rank rows per expert.  Quantised by default
+    num_experts)): one launch, no layout call, into the capacity-padded buffer
+    of num_max_dispatch_tokens_per_rank rows per expert.  Quantised by default
     (e4m3 with one fp32 scale per 128 channels); quant="bf16" turns it off.
+    The same slots, codes and scales as get_dispatch_layout + dispatch with
+    recv_layout="padded"; built for decode batches (T*K <= 4096, K <= 64),
+    beyond which the library reports the request as unsupported and that pair
+    is the call to use.
     -> (recv_x [E, cap, H or H/2], recv_scales [E, cap, ...] or None, Handle);
-    the shapes are views of the flat receive rows."""
+    the shapes are views of the flat receive rows, and handle.recv_count [E]
+    holds the rows each expert received (at most cap)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    T, H = x.shape
+    if topk_idx.shape[0] != T:
+        raise ValueError("x and topk_idx disagree on the number of tokens")
+    K = topk_idx.shape[1]
     E, cap = int(num_experts), int(num_max_dispatch_tokens_per_rank)
-    L = get_dispatch_layout(topk_idx, E)
-    recv, scales, h = dispatch(x, L, quant=quant, recv_layout="padded", cap=cap)
+    quant = _QUANT_ALIASES.get(quant, quant)
+    if quant not in _QUANT:
+        raise ValueError(f"unknown quant mode {quant!r}")
+    q, rdt, row_div, scale_shape = _QUANT[quant]
+    if E < 1 or cap < 0:
+        raise ValueError("num_experts must be >= 1 and the capacity >= 0")
+    rows = E * cap
+    dev = x.device
+    _same_device(dev, topk_idx=topk_idx)
+    recv = torch.empty((rows, H // row_div), dtype=rdt, device=dev)
+    scales = None
+    if scale_shape is not None:
+        ncol, sdt = scale_shape(H)
+        scales = torch.empty((rows, ncol) if ncol else (rows,), dtype=sdt, device=dev)
+    slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+    src = torch.empty(rows, dtype=torch.int32, device=dev)
+    cnt = torch.empty(E, dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        N.ep_low_latency_dispatch(_ptr(x), T, H, _ptr(topk_idx), K, E, cap, q, _ptr(recv),
+                                  _ptr(scales), _ptr(slot), _ptr(src), _ptr(cnt), _ptr(nd),
+                                  _ptr(ninv), _stream(dev))
     recv = recv.view(E, cap, *recv.shape[1:])
     if scales is not None:
         scales = scales.view(E, cap, *scales.shape[1:])
-    return recv, scales, h
+    return recv, scales, Handle(slot, src, nd, rows, "padded", cap, cnt, ninv)
 
 
 def low_latency_combine(y: torch.Tensor, topk_idx: torch.Tensor,

@@ -140,6 +140,43 @@ ep_status_t ep_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx
                                           static_cast<hipStream_t>(stream)));
 }
 
+ep_status_t ep_low_latency_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx,
+                                    int K, int E, int cap, ep_quant_t quant, void *recv_x,
+                                    void *recv_scales, int32_t *slot, int32_t *recv_src,
+                                    int32_t *recv_count, int32_t *num_dropped,
+                                    int32_t *num_invalid, void *stream)
+{
+    ep_status_t st = check_layout_sizes(T, K, E, 1);
+    if (st != EP_OK)
+        return st;
+    if ((int)quant < (int)EP_QUANT_BF16 || (int)quant > (int)EP_QUANT_MXFP4_E2M1)
+        return EP_ERR_INVALID_ARG;
+    const bool quantised = quant != EP_QUANT_BF16;
+    const bool mx = quant == EP_QUANT_MXFP8_E4M3 || quant == EP_QUANT_MXFP8_E5M2 ||
+                    quant == EP_QUANT_MXFP4_E2M1;
+    if (H < 8 || H % 8 != 0 || (quant == EP_QUANT_FP8_E4M3_G128 && H % 128 != 0) ||
+        (mx && H % 32 != 0))
+        return EP_ERR_INVALID_ARG;
+    if (H > kMaxHidden)
+        return EP_ERR_UNSUPPORTED;
+    if (cap < 0 || (int64_t)E * cap > kI32)
+        return EP_ERR_INVALID_ARG;
+    if (!ep::ll_dispatch_fits(T, K, H, (int)quant))
+        return EP_ERR_UNSUPPORTED;
+    const bool rows = (int64_t)E * cap > 0;
+    if (!recv_count || !num_dropped || !num_invalid || (T > 0 && (!x || !topk_idx || !slot)) ||
+        (rows && T > 0 && !recv_x) || (quantised && rows && T > 0 && !recv_scales))
+        return EP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || (!mx && !aligned(recv_scales, 4)) ||
+        !aligned(topk_idx, 4) || !aligned(slot, 4) || !aligned(recv_src, 4) ||
+        !aligned(recv_count, 4) || !aligned(num_dropped, 4) || !aligned(num_invalid, 4))
+        return EP_ERR_INVALID_ARG;
+    return hip_status(ep::launch_ll_dispatch(x, T, H, topk_idx, K, E, cap, (int)quant, recv_x,
+                                             recv_scales, slot, recv_src, recv_count,
+                                             num_dropped, num_invalid,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 ep_status_t ep_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot,
                        const float *topk_weights, int T, int K, uint16_t *out, void *stream)
 {

@@ -59,6 +59,76 @@ __global__ void dropped_only_kernel(const int32_t *__restrict__ offsets, int E, 
     write_num_dropped(offsets, E, padded, cap_or_rows, num_dropped);
 }
 
+// n ints from global to shared memory by the whole block, 8 loads in flight
+// per thread (one memory round trip per 8 * blockDim.x entries).
+__device__ __forceinline__ void stage_ints(const int32_t *__restrict__ src, int n,
+                                           int32_t *__restrict__ dst)
+{
+    for (int i0 = 0; i0 < n; i0 += 8 * blockDim.x) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * blockDim.x + threadIdx.x;
+            v[u] = i < n ? src[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * blockDim.x + threadIdx.x;
+            if (i < n)
+                dst[i] = v[u];
+        }
+    }
+}
+
+// The one-launch low-latency form's per-expert results, from one block: an
+// LDS histogram of all n entries gives the rows each expert received
+// (capped at cap), the entries dropped for capacity, and the invalid ones.
+__device__ void ll_counts(const int32_t *topk_idx, int n, int E, int cap, int32_t *ent,
+                          int32_t *hist, int32_t *recv_count, int32_t *num_dropped,
+                          int32_t *num_invalid)
+{
+    __shared__ int tmp[32];
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        hist[e] = 0;
+    stage_ints(topk_idx, n, ent);
+    __syncthreads();
+    int inval = 0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int v = ent[i];
+        if ((unsigned)v < (unsigned)E)
+            atomicAdd(&hist[v], 1);
+        else if (v != -1)
+            ++inval;
+    }
+    __syncthreads();
+    int d = 0;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const int c = hist[e];
+        recv_count[e] = c < cap ? c : cap;
+        d += c > cap ? c - cap : 0;
+    }
+    int total;
+    block_exclusive_scan(d, tmp, &total);
+    if (threadIdx.x == 0)
+        num_dropped[0] = total;
+    block_exclusive_scan(inval, tmp, &total);
+    if (threadIdx.x == 0)
+        num_invalid[0] = total;
+}
+
+// The low-latency form with no tokens: every count is zero.
+__global__ void ll_empty_kernel(int E, int32_t *__restrict__ recv_count,
+                                int32_t *__restrict__ num_dropped,
+                                int32_t *__restrict__ num_invalid)
+{
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        recv_count[e] = 0;
+    if (threadIdx.x == 0) {
+        num_dropped[0] = 0;
+        num_invalid[0] = 0;
+    }
+}
+
 constexpr bool is_token_mode(int m) { return m == kQuantFp8Token || m == kQuantInt8Token; }
 constexpr bool is_mx_mode(int m)
 {
@@ -229,24 +299,45 @@ __device__ __forceinline__ void store_unit(rsrc_t dst, int i, int units, int H, 
 // One block per (token, row segment).  A thread handles PPT units of U
 // adjacent 16-byte pieces (U = 2 for the 8-bit codes when the row has an
 // even number of pieces, so that a lane stores 16 bytes of codes).
-template <int PPT, int MODE, int U>
+//
+// LL (the one-launch low-latency form, padded rows, K <= 64): there is no
+// layout call.  Each block stages topk_idx up to its own token in shared
+// memory (dynamic: T*K entries, 64 rank counters, and E histogram bins for
+// the count block) and ranks its token's entries itself: the rank of (t,k) is the
+// number of entries before it in row-major order with the same expert, the
+// same stable counting sort the layout performs.  One more block (grid.x =
+// T + 1) writes the per-expert received counts, the dropped and the invalid
+// counts.
+template <int PPT, int MODE, int U, bool LL>
 __global__ void __launch_bounds__(256)
 dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict__ topk_idx, int K,
                 int E, const int32_t *__restrict__ offsets, int padded, int cap_or_rows, int CT,
                 int nchunk, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ local_rank,
                 void *__restrict__ recv_x, void *__restrict__ recv_s,
                 int32_t *__restrict__ slot_out, int32_t *__restrict__ recv_src,
-                int32_t *__restrict__ num_dropped, const float *__restrict__ tok_amax)
+                int32_t *__restrict__ num_dropped, const float *__restrict__ tok_amax,
+                int32_t *__restrict__ recv_count, int32_t *__restrict__ num_invalid)
 {
     constexpr bool QUANT = MODE != kQuantBf16;
     static_assert(U == 1 || (U == 2 && QUANT), "pairs are for the quantised modes");
+    extern __shared__ int32_t ll_lds[];
     const int t = blockIdx.x;
     const int tid = threadIdx.x, bd = blockDim.x;
     const int pieces = H >> 3;
     const int units = pieces / U;
     const int seg0 = blockIdx.y * PPT * bd;
-    if (t == 0 && blockIdx.y == 0)
+    if constexpr (LL) {
+        // the last block of the grid only counts (in parallel with the tokens)
+        const int T = (int)gridDim.x - 1;
+        if (t == T) {
+            if (blockIdx.y == 0)
+                ll_counts(topk_idx, T * K, E, cap_or_rows, ll_lds, ll_lds + T * K + 64,
+                          recv_count, num_dropped, num_invalid);
+            return;
+        }
+    } else if (t == 0 && blockIdx.y == 0) {
         write_num_dropped(offsets, E, padded, cap_or_rows, num_dropped);
+    }
 
     const char *xrow = reinterpret_cast<const char *>(x) + (size_t)t * H * 2;
     u32x4 v[PPT][U];
@@ -256,6 +347,46 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
 #pragma unroll
         for (int h = 0; h < U; ++h)
             v[j][h] = i < units ? ld16(xrow + ((size_t)i * U + h) * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // LL: lane k's rank (k < K <= 64), counted while the row is in flight.
+    // For each of the token's experts, every thread compares the earlier
+    // entries at its positions (4 per round, read together), each wave sums
+    // its matches with ballots and popcounts, and adds them to the expert's
+    // counter in shared memory.  The staged entries also give the experts to
+    // the slot loop below, with no second global load.
+    int ll_rank = 0;
+    if constexpr (LL) {
+        const int n = (t + 1) * K;
+        int32_t *rk = ll_lds + ((int)gridDim.x - 1) * K;
+        stage_ints(topk_idx, n, ll_lds);
+        if (tid < K)
+            rk[tid] = 0;
+        __syncthreads();
+        const int lane = tid & (kWave - 1);
+        const int ek = lane < K ? ll_lds[t * K + lane] : -1;
+        for (int k = 0; k < K; ++k) {
+            const int e = __builtin_amdgcn_readlane(ek, k);
+            if ((unsigned)e >= (unsigned)E)
+                continue;
+            const int lim = t * K + k;
+            int cnt = 0;
+            for (int i0 = 0; i0 < lim; i0 += 4 * bd) {
+                bool hit[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {          // 4 shared-memory reads in flight
+                    const int i = i0 + u * bd + tid;
+                    hit[u] = ll_lds[i < lim ? i : 0] == e && i < lim;   // lim >= 1
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    cnt += __builtin_popcountll(ballot(hit[u]));
+            }
+            if (lane == 0 && cnt)
+                atomicAdd(&rk[k], cnt);
+        }
+        __syncthreads();
+        ll_rank = lane < K ? rk[lane] : 0;
     }
 
     // q: the unit's codes (8U bytes, or 4U for e2m1); sc: its group's scale
@@ -302,7 +433,7 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
     // handle.  The stores then take each slot with readlane.
     const int c = t / CT;
     const int32_t *trow = topk_idx + (int64_t)t * K;
-    const int32_t *rrow = local_rank + (int64_t)t * K;
+    const int32_t *rrow = LL ? nullptr : local_rank + (int64_t)t * K;
     const int64_t rb = row_bytes(MODE, H);
     const int lane = tid & (kWave - 1);
     const bool writer = blockIdx.y == 0 && tid < kWave;
@@ -311,9 +442,13 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
         const int k = k0 + lane;
         int sl = -1;
         if (k < K) {
-            const int e = trow[k];
+            const int e = LL ? ll_lds[t * K + k] : trow[k];   // LL: staged with the rest
             if ((unsigned)e < (unsigned)E) {
-                const int r = chunk_base[(int64_t)e * nchunk + c] + rrow[k];
+                int r;
+                if constexpr (LL)
+                    r = ll_rank;                       // k == lane: K <= 64
+                else
+                    r = chunk_base[(int64_t)e * nchunk + c] + rrow[k];
                 if (padded)
                     sl = r < cap_or_rows ? e * cap_or_rows + r : -1;
                 else {
@@ -398,17 +533,18 @@ RowShape row_shape(int pieces, int maxppt = 8)
     return best;
 }
 
-template <int MODE, int U>
+template <int MODE, int U, bool LL>
 hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint16_t *x, int H,
                              const int32_t *topk_idx, const int32_t *offsets, int padded,
                              int cap_or_rows, void *recv_x, void *recv_s, int32_t *slot,
                              int32_t *recv_src, int32_t *num_dropped, const int32_t *hist,
-                             const int32_t *rank, float *tamax_ws, hipStream_t s)
+                             const int32_t *rank, float *tamax_ws, int32_t *recv_count,
+                             int32_t *num_invalid, size_t lds, hipStream_t s)
 {
     // A per-token scale needs the whole row's max; when the row spans several
     // blocks it is taken first, into the workspace.
     float *tok_amax = nullptr;
-    if (is_token_mode(MODE) && rs.nseg != 1) {
+    if (!LL && is_token_mode(MODE) && rs.nseg != 1) {
         tok_amax = tamax_ws;
         hipLaunchKernelGGL(token_amax_kernel, dim3(p.T), dim3(256), 0, s, x, H, tok_amax);
         hipError_t err = hipGetLastError();
@@ -417,30 +553,91 @@ hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint
     }
     if ((uint64_t)p.T * rs.bd > 0xFFFFFFFFull)    // work-items per grid dimension fit 32 bits
         return hipErrorInvalidConfiguration;
-    dim3 grid(p.T, rs.nseg), block(rs.bd);
+    dim3 grid(p.T + (LL ? 1 : 0), rs.nseg), block(rs.bd);
 #define EP_DISPATCH_CASE(N)                                                                      \
     case N:                                                                                      \
-        hipLaunchKernelGGL((dispatch_kernel<N, MODE, U>), grid, block, 0, s, x, H, topk_idx, p.K, \
-                           p.E, offsets, padded, cap_or_rows, p.CT, p.nchunk, hist, rank,       \
-                           recv_x, recv_s, slot, recv_src, num_dropped, tok_amax);               \
+        hipLaunchKernelGGL((dispatch_kernel<N, MODE, U, LL>), grid, block, lds, s, x, H,         \
+                           topk_idx, p.K, p.E, offsets, padded, cap_or_rows, p.CT, p.nchunk,     \
+                           hist, rank, recv_x, recv_s, slot, recv_src, num_dropped, tok_amax,    \
+                           recv_count, num_invalid);                                             \
         break;
-    switch (rs.ppt) {
-        EP_DISPATCH_CASE(1)
-        EP_DISPATCH_CASE(2)
-        EP_DISPATCH_CASE(3)
-        EP_DISPATCH_CASE(4)
-        EP_DISPATCH_CASE(5)
-        EP_DISPATCH_CASE(6)
-        EP_DISPATCH_CASE(7)
-        EP_DISPATCH_CASE(8)
-    default:
-        return hipErrorInvalidValue;
+    if constexpr (LL) {          // at most 2 units per thread (launch_ll_dispatch)
+        switch (rs.ppt) {
+            EP_DISPATCH_CASE(1)
+            EP_DISPATCH_CASE(2)
+        default:
+            return hipErrorInvalidValue;
+        }
+    } else {
+        switch (rs.ppt) {
+            EP_DISPATCH_CASE(1)
+            EP_DISPATCH_CASE(2)
+            EP_DISPATCH_CASE(3)
+            EP_DISPATCH_CASE(4)
+            EP_DISPATCH_CASE(5)
+            EP_DISPATCH_CASE(6)
+            EP_DISPATCH_CASE(7)
+            EP_DISPATCH_CASE(8)
+        default:
+            return hipErrorInvalidValue;
+        }
     }
 #undef EP_DISPATCH_CASE
     return hipGetLastError();
 }
 
+// Units per row: 8-bit codes of rows with an even number of pieces go in
+// pairs of pieces (16-byte stores; measured at prefill: fp8 per 128 channels
+// 63 -> 56 us, MXFP8 71 -> 54 us); e2m1 stays at one piece (4-byte stores
+// measured faster than 8-byte ones there: 31 vs 33 us).
+bool pairs_for(int quant, int H)
+{
+    return quant != kQuantBf16 && quant != kQuantMxE2M1 && (H / 8) % 2 == 0;
+}
+
+// The low-latency form's block shape: 256 threads, at most 2 units per
+// thread, as few row segments as that allows (each segment's block repeats
+// the token's ranking, which 256 threads share); a per-token row must fit
+// one block (nseg = 0: too long).  Measured at decode (T = 128, H = 7168):
+// bf16 rows (896 units) over 7 one-wave blocks took 13.4 us for the
+// dispatch (events), over 2 blocks of 256 threads 10.3 us.
+RowShape ll_shape(int quant, int H)
+{
+    const int units = pairs_for(quant, H) ? H / 16 : H / 8;
+    const int ppt = units <= 256 ? 1 : 2;
+    const int nseg = (units + 2 * 256 - 1) / (2 * 256);
+    if (is_token_mode(quant) && nseg != 1)
+        return {256, 2, 0};
+    return {256, ppt, nseg};
+}
+
 }  // namespace
+
+// Launch of the dispatch kernel for one mode, with or without pairs of
+// pieces per unit.
+#define EP_MODE_SWITCH(LL, ...)                                                                  \
+    do {                                                                                         \
+        if (!pairs) {                                                                            \
+            switch (quant) {                                                                     \
+            case kQuantBf16: return launch_dispatch_t<kQuantBf16, 1, LL>(__VA_ARGS__);           \
+            case kQuantFp8G128: return launch_dispatch_t<kQuantFp8G128, 1, LL>(__VA_ARGS__);     \
+            case kQuantFp8Token: return launch_dispatch_t<kQuantFp8Token, 1, LL>(__VA_ARGS__);   \
+            case kQuantInt8Token: return launch_dispatch_t<kQuantInt8Token, 1, LL>(__VA_ARGS__); \
+            case kQuantMxE4M3: return launch_dispatch_t<kQuantMxE4M3, 1, LL>(__VA_ARGS__);       \
+            case kQuantMxE5M2: return launch_dispatch_t<kQuantMxE5M2, 1, LL>(__VA_ARGS__);       \
+            case kQuantMxE2M1: return launch_dispatch_t<kQuantMxE2M1, 1, LL>(__VA_ARGS__);       \
+            default: return hipErrorInvalidValue;                                                \
+            }                                                                                    \
+        }                                                                                        \
+        switch (quant) {                                                                         \
+        case kQuantFp8G128: return launch_dispatch_t<kQuantFp8G128, 2, LL>(__VA_ARGS__);         \
+        case kQuantFp8Token: return launch_dispatch_t<kQuantFp8Token, 2, LL>(__VA_ARGS__);       \
+        case kQuantInt8Token: return launch_dispatch_t<kQuantInt8Token, 2, LL>(__VA_ARGS__);     \
+        case kQuantMxE4M3: return launch_dispatch_t<kQuantMxE4M3, 2, LL>(__VA_ARGS__);           \
+        case kQuantMxE5M2: return launch_dispatch_t<kQuantMxE5M2, 2, LL>(__VA_ARGS__);           \
+        default: return hipErrorInvalidValue;                                                    \
+        }                                                                                        \
+    } while (0)
 
 hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const int32_t *topk_idx,
                            const int32_t *offsets, bool padded, int cap_or_rows, int quant,
@@ -455,48 +652,53 @@ hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const 
                            (int)padded, cap_or_rows, num_dropped);
         return hipGetLastError();
     }
-    // 8-bit codes of rows with an even number of pieces go in pairs of pieces
-    // (16-byte stores; measured at prefill: fp8 per 128 channels 63 -> 56 us,
-    // MXFP8 71 -> 54 us); e2m1 stays at one piece (4-byte stores measured
-    // faster than 8-byte ones there: 31 vs 33 us)
-    const bool pairs = quant != kQuantBf16 && quant != kQuantMxE2M1 && (H / 8) % 2 == 0;
+    const bool pairs = pairs_for(quant, H);
     // Few tokens (a latency-bound launch): at most 2 units per thread, so a
     // row spreads over more threads.  Measured at decode (T = 128, H = 7168):
     // fp8 per 128 channels 20.6 -> 10.4 us, MXFP8 15.8 -> 9.6 us, bf16 about
     // the same.  A per-token row must stay in one block.
     const int units = pairs ? H / 16 : H / 8;
     RowShape rs = row_shape(units, p.T < 1024 ? 2 : 8);
-    const bool per_token = quant == kQuantFp8Token || quant == kQuantInt8Token;
-    if (per_token && rs.nseg != 1)
+    if (is_token_mode(quant) && rs.nseg != 1)
         rs = row_shape(units, 8);
-#define EP_MODE_CASE(M, UU)                                                                      \
-    case M:                                                                                      \
-        return launch_dispatch_t<M, UU>(p, rs, x, H, topk_idx, offsets, padded, cap_or_rows,     \
-                                        recv_x, recv_scales, slot, recv_src, num_dropped, hist,  \
-                                        rank, tamax, s);
-    if (!pairs) {
-        switch (quant) {
-            EP_MODE_CASE(kQuantBf16, 1)
-            EP_MODE_CASE(kQuantFp8G128, 1)
-            EP_MODE_CASE(kQuantFp8Token, 1)
-            EP_MODE_CASE(kQuantInt8Token, 1)
-            EP_MODE_CASE(kQuantMxE4M3, 1)
-            EP_MODE_CASE(kQuantMxE5M2, 1)
-            EP_MODE_CASE(kQuantMxE2M1, 1)
-        default:
-            return hipErrorInvalidValue;
-        }
-    }
-    switch (quant) {
-        EP_MODE_CASE(kQuantFp8G128, 2)
-        EP_MODE_CASE(kQuantFp8Token, 2)
-        EP_MODE_CASE(kQuantInt8Token, 2)
-        EP_MODE_CASE(kQuantMxE4M3, 2)
-        EP_MODE_CASE(kQuantMxE5M2, 2)
-    default:
-        return hipErrorInvalidValue;
-    }
-#undef EP_MODE_CASE
+    EP_MODE_SWITCH(false, p, rs, x, H, topk_idx, offsets, (int)padded, cap_or_rows, recv_x,
+                   recv_scales, slot, recv_src, num_dropped, hist, rank, tamax, nullptr, nullptr,
+                   0, s);
 }
+
+bool ll_dispatch_fits(int T, int K, int H, int quant)
+{
+    return (int64_t)T * K <= kLlMaxEntries && K <= kLlMaxTopk && ll_shape(quant, H).nseg > 0;
+}
+
+hipError_t launch_ll_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx, int K,
+                              int E, int cap, int quant, void *recv_x, void *recv_scales,
+                              int32_t *slot, int32_t *recv_src, int32_t *recv_count,
+                              int32_t *num_dropped, int32_t *num_invalid, hipStream_t s)
+{
+    if (!ll_dispatch_fits(T, K, H, quant))
+        return hipErrorInvalidValue;
+    if (T == 0) {
+        hipLaunchKernelGGL(ll_empty_kernel, dim3(1), dim3(256), 0, s, E, recv_count, num_dropped,
+                           num_invalid);
+        return hipGetLastError();
+    }
+    // no chunk tables: one chunk, ranks found in the kernel
+    LayoutPlan p{};
+    p.T = T;
+    p.K = K;
+    p.E = E;
+    p.R = 1;
+    p.CT = T;
+    p.nchunk = 1;
+    const bool pairs = pairs_for(quant, H);
+    const RowShape rs = ll_shape(quant, H);
+    // the staged entries, the token's rank counters, the count block's histogram
+    const size_t lds = ((size_t)T * K + 64 + E) * sizeof(int32_t);
+    EP_MODE_SWITCH(true, p, rs, x, H, topk_idx, nullptr, 1, cap, recv_x, recv_scales, slot,
+                   recv_src, num_dropped, nullptr, nullptr, nullptr, recv_count, num_invalid, lds,
+                   s);
+}
+#undef EP_MODE_SWITCH
 
 }  // namespace ep

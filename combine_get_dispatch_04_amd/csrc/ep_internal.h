@@ -49,6 +49,17 @@ hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const 
                            void *recv_x, void *recv_scales, int32_t *slot, int32_t *recv_src,
                            int32_t *num_dropped, char *ws, hipStream_t s);
 
+// The one-launch low-latency dispatch (padded rows, ranks found in the
+// kernel): each block scans the entries before its token, so it is built for
+// small batches.
+constexpr int kLlMaxEntries = 4096;   // T*K
+constexpr int kLlMaxTopk = 64;        // one lane per (t,k)
+bool ll_dispatch_fits(int T, int K, int H, int quant);
+hipError_t launch_ll_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx, int K,
+                              int E, int cap, int quant, void *recv_x, void *recv_scales,
+                              int32_t *slot, int32_t *recv_src, int32_t *recv_count,
+                              int32_t *num_dropped, int32_t *num_invalid, hipStream_t s);
+
 hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot,
                           const float *w, int T, int K, uint16_t *out, hipStream_t s);
 

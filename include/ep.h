@@ -183,6 +183,32 @@ ep_status_t ep_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx
                         void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * ep_low_latency_dispatch -- [EPA] API Overview, low_latency_dispatch(x,
+ * topk_idx, num_max_dispatch_tokens_per_rank, num_experts): the decode-phase
+ * dispatch into the capacity-padded buffer, in one launch, with no layout
+ * call and no workspace.  slot, recv_x, recv_scales, recv_src and
+ * num_dropped are exactly those of ep_get_dispatch_layout followed by
+ * ep_dispatch with EP_LAYOUT_PADDED and cap_or_max_rows = cap (same
+ * arguments, same quantisation modes); in addition
+ *   recv_count   [E] int32 out: min(cap, valid (t,k) with expert e), the
+ *                rows of expert e that hold a token (rows e*cap ..
+ *                e*cap + recv_count[e] - 1).
+ *   num_invalid  [1] int32 out: entries neither -1 nor in [0, E).
+ * Each block ranks its own token's entries by counting equal experts among
+ * the entries before them, so the work grows as (T*K)^2: built for decode
+ * batches.  Limits (EP_ERR_UNSUPPORTED beyond them; the layout + dispatch
+ * pair has none of them): T*K <= 4096, K <= 64, and for the per-token modes
+ * a row of at most 512 units of 16 channels (H <= 8192 when H/8 is even,
+ * else H <= 4096).  Other constraints as ep_dispatch, with 1 <= E <= 4096,
+ * cap >= 0 and E*cap < 2^31.
+ */
+ep_status_t ep_low_latency_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx,
+                                    int K, int E, int cap, ep_quant_t quant, void *recv_x,
+                                    void *recv_scales, int32_t *slot, int32_t *recv_src,
+                                    int32_t *recv_count, int32_t *num_dropped,
+                                    int32_t *num_invalid, void *stream);
+
+/*
  * ep_combine -- [EPA] API Overview, combine (reduce through the dispatch
  * handle) and low_latency_combine (also takes topk_weights).
  *   out[t, :] = bf16( sum over k with slot[t,k] >= 0 of w[t,k] * y[slot[t,k], :] )

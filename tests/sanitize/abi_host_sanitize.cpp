@@ -1,7 +1,7 @@
 // Host-side paths of the C ABI (include/ep.h) that run without a GPU: the
 // workspace sizing of ep_workspace_bytes / ep_ec_workspace_bytes over a wide
 // grid of sizes, up to T*K and E*C near 2^31, and the argument checks of all
-// five entry points, which must return their status before anything is
+// six entry points, which must return their status before anything is
 // enqueued.  Built with the host pass under AddressSanitizer and
 // UndefinedBehaviorSanitizer, so that an overflow in the size arithmetic or
 // an access outside a host object is reported.  Exit status 0 = clean.
@@ -89,6 +89,29 @@ int main()
                        i4, i4, i4, ws, sizeof ws, nullptr) == inval, "dispatch: layout enum", 7, 0);
     expect(ep_dispatch(h2, 4, 64, i4, 2, 8, i4, EP_LAYOUT_CONTIGUOUS, 8, (ep_quant_t)9, h2, nullptr,
                        i4, i4, i4, ws, sizeof ws, nullptr) == inval, "dispatch: quant enum", 9, 0);
+    // the one-launch low-latency dispatch: limits and argument checks
+    expect(ep_low_latency_dispatch(h2, 4097, 64, i4, 1, 8, 4, EP_QUANT_BF16, h2, nullptr, i4, i4,
+                                   i4, i4, i4, nullptr) == unsup, "ll: T*K beyond 4096", 4097, 1);
+    expect(ep_low_latency_dispatch(h2, 1, 64, i4, 65, 8, 4, EP_QUANT_BF16, h2, nullptr, i4, i4, i4,
+                                   i4, i4, nullptr) == unsup, "ll: K beyond 64", 1, 65);
+    expect(ep_low_latency_dispatch(h2, 4, 8320, i4, 2, 8, 4, EP_QUANT_INT8_TOKEN, u1, f4, i4, i4,
+                                   i4, i4, i4, nullptr) == unsup, "ll: per-token row of 520 pairs",
+           8320, 0);
+    expect(ep_low_latency_dispatch(h2, 4, 4104, i4, 2, 8, 4, EP_QUANT_FP8_E4M3_TOKEN, u1, f4, i4,
+                                   i4, i4, i4, i4, nullptr) == unsup,
+           "ll: per-token row of 513 pieces", 4104, 0);
+    expect(ep_low_latency_dispatch(h2, 4, 64, i4, 2, 8, -1, EP_QUANT_BF16, h2, nullptr, i4, i4, i4,
+                                   i4, i4, nullptr) == inval, "ll: cap < 0", -1, 0);
+    expect(ep_low_latency_dispatch(h2, 4, 64, i4, 2, 4096, 1 << 20, EP_QUANT_BF16, h2, nullptr, i4,
+                                   i4, i4, i4, i4, nullptr) == inval, "ll: E*cap beyond 2^31", 0, 0);
+    expect(ep_low_latency_dispatch(h2, 4, 64, i4, 2, 8, 4, 9, h2, nullptr, i4, i4, i4, i4, i4,
+                                   nullptr) == inval, "ll: quant code", 9, 0);
+    expect(ep_low_latency_dispatch(h2, 4, 64, i4, 2, 8, 4, EP_QUANT_FP8_E4M3_G128, u1, f4, i4, i4,
+                                   i4, i4, i4, nullptr) == inval, "ll: fp8 H % 128", 64, 0);
+    expect(ep_low_latency_dispatch(h2, 4, 64, i4, 2, 8, 4, EP_QUANT_BF16, h2, nullptr, i4, i4,
+                                   nullptr, i4, i4, nullptr) == inval, "ll: null recv_count", 0, 0);
+    expect(ep_low_latency_dispatch(h2, 4, 64, i4, 2, 5000, 4, EP_QUANT_BF16, h2, nullptr, i4, i4,
+                                   i4, i4, i4, nullptr) == unsup, "ll: E beyond 4096", 5000, 0);
     expect(ep_combine(h2, 8, 64, i4, f4, -1, 2, h2, nullptr) == inval, "combine: T < 0", 0, 0);
     expect(ep_combine(h2, 8, 64, nullptr, f4, 4, 2, h2, nullptr) == inval, "combine: null slot", 0, 0);
     expect(ep_combine(h2, 8, 64, i4, f4, 1 << 30, 8, h2, nullptr) == inval, "combine: T*K beyond 2^31", 0, 0);

@@ -27,10 +27,10 @@ def _declared():
     return out
 
 
-def test_header_declares_the_five_operations():
+def test_header_declares_the_operations():
     d = _declared()
-    for name in ("ep_get_dispatch_layout", "ep_dispatch", "ep_combine",
-                 "ep_dispatch_expert_choice", "ep_combine_expert_choice"):
+    for name in ("ep_get_dispatch_layout", "ep_dispatch", "ep_low_latency_dispatch",
+                 "ep_combine", "ep_dispatch_expert_choice", "ep_combine_expert_choice"):
         assert name in d
 
 
@@ -137,6 +137,38 @@ def _dispatch(**kw):
 ])
 def test_dispatch_rejects(kw, status):
     assert _dispatch(**kw) == status
+
+
+def _ll(**kw):
+    args = dict(x=A, T=16, H=256, topk_idx=A, K=2, E=8, cap=4, quant=0, recv_x=B,
+                recv_scales=None, slot=A, recv_src=A, recv_count=A, num_dropped=A,
+                num_invalid=A, stream=None)
+    args.update(kw)
+    return N.ep_low_latency_dispatch(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=4097, K=1), N.EP_ERR_UNSUPPORTED),                      # T*K beyond 4096
+    (dict(T=1, K=65), N.EP_ERR_UNSUPPORTED),                        # K beyond 64
+    (dict(quant=3, H=8320, recv_scales=A), N.EP_ERR_UNSUPPORTED),   # per-token row of 520 pairs
+    (dict(quant=2, H=4104, recv_scales=A), N.EP_ERR_UNSUPPORTED),   # 513 single pieces
+    (dict(E=9000), N.EP_ERR_UNSUPPORTED),
+    (dict(cap=-1), N.EP_ERR_INVALID_ARG),
+    (dict(E=4096, cap=1 << 20), N.EP_ERR_INVALID_ARG),              # E*cap >= 2^31
+    (dict(quant=7), N.EP_ERR_INVALID_ARG),
+    (dict(quant=1, H=200, recv_scales=A), N.EP_ERR_INVALID_ARG),
+    (dict(quant=1, recv_scales=None), N.EP_ERR_INVALID_ARG),
+    (dict(H=12), N.EP_ERR_INVALID_ARG),
+    (dict(x=A + 8), N.EP_ERR_INVALID_ARG),
+    (dict(recv_count=None), N.EP_ERR_INVALID_ARG),
+    (dict(num_invalid=None), N.EP_ERR_INVALID_ARG),
+    (dict(num_dropped=None), N.EP_ERR_INVALID_ARG),
+    (dict(slot=None), N.EP_ERR_INVALID_ARG),
+    (dict(recv_x=None), N.EP_ERR_INVALID_ARG),
+    (dict(K=0), N.EP_ERR_INVALID_ARG),
+])
+def test_low_latency_dispatch_rejects(kw, status):
+    assert _ll(**kw) == status
 
 
 @pytest.mark.parametrize("kw,status", [

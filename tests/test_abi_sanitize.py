@@ -2,7 +2,7 @@
 
 tests/sanitize/abi_host_sanitize.cpp drives every host path of libep that
 runs without a GPU: the workspace sizing over a wide grid of shapes (T*K and
-E*C up to just below 2^31) and the argument checks of the five entry points.
+E*C up to just below 2^31) and the argument checks of the six entry points.
 The library sources and the driver are built by hipcc with the sanitizers on
 the host pass only (each -fsanitize= after -Xarch_host; the gfx950 code is
 built as usual) and the run must be clean.  A copy of ep_api.hip that

@@ -179,6 +179,7 @@ def test_low_latency_pair(quant):
     torch.cuda.synchronize()
     assert np.array_equal(G.host(h.slot), s_ref)
     assert int(G.host(h.num_dropped)[0]) == nd_ref
+    assert np.array_equal(G.host(h.recv_count), np.minimum(oracle.layout(c.topk_idx, c.E)["counts"], cap))
     m = _written(s_ref, rows)
     if quant == "bf16":
         y = oracle.dispatch_bf16(c.x, s_ref, rows)

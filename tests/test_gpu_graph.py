@@ -1,8 +1,9 @@
 """The hot path captured in a HIP graph and replayed.
 
-Layout, dispatch and combine (and the expert-choice pair) are recorded once
-through the torch front end (the C ABI enqueues everything on the current
-stream, allocates nothing and issues no memset), then the graph is replayed
+Layout, dispatch and combine (and the expert-choice and low-latency pairs)
+are recorded once through the torch front end (the C ABI enqueues
+everything on the current stream, allocates nothing and issues no memset),
+then the graph is replayed
 with new inputs copied into its static tensors.  Between replays the same
 calls run eagerly on the new inputs, with synchronisations, and every replay
 must give the eager results bit for bit.
@@ -125,3 +126,50 @@ def test_expert_choice_graph_replays(T, H, E, C):
         assert torch.equal(graph_out[2].reshape(E * C, H)[filled].view(torch.int16),
                            eager[2].reshape(E * C, H)[filled].view(torch.int16)), r
         assert torch.equal(graph_out[3].view(torch.int16), eager[3].view(torch.int16)), r
+
+
+# (T, H, E, K, cap, quant): the decode shape with overflow, fp8 and bf16
+LL_GRAPH = [(128, 7168, 256, 8, 6, "fp8_e4m3_g128"), (96, 1024, 32, 6, 16, "bf16")]
+
+
+@pytest.mark.parametrize("T,H,E,K,cap,quant", LL_GRAPH)
+def test_low_latency_graph_replays(T, H, E, K, cap, quant):
+    """low_latency_dispatch (one launch) + low_latency_combine captured."""
+    def step(x, idx, w):
+        recv, scales, h = api.low_latency_dispatch(x, idx, cap, E, quant=quant)
+        out = api.low_latency_combine(recv, idx, w, h) if quant == "bf16" else None
+        return dict(slot=h.slot, recv_src=h.recv_src, cnt=h.recv_count, nd=h.num_dropped,
+                    ninv=h.num_invalid, recv=recv.reshape(E * cap, -1),
+                    scales=None if scales is None else scales.reshape(E * cap, -1), out=out)
+
+    x_s, idx_s, w_s = _dev_tc(W.random_token_choice(90, T, H, E, K, p_pad=0.1, p_invalid=0.02))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(x_s, idx_s, w_s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        go = step(x_s, idx_s, w_s)
+    b = lambda t: t.view(torch.uint8)
+    for r in range(REPLAYS):
+        x, idx, w = _dev_tc(W.random_token_choice(100 + r, T, H, E, K, p_pad=0.1,
+                                                  p_invalid=0.02, p_dup=0.1))
+        x_s.copy_(x)
+        idx_s.copy_(idx)
+        w_s.copy_(w)
+        g.replay()
+        torch.cuda.synchronize()
+        e = step(x, idx, w)
+        torch.cuda.synchronize()
+        for k in ("slot", "cnt", "nd", "ninv"):
+            assert torch.equal(go[k], e[k]), (r, k)
+        kept = e["slot"][e["slot"] >= 0].long()
+        assert torch.equal(go["recv_src"][kept], e["recv_src"][kept]), r
+        assert torch.equal(b(go["recv"][kept]), b(e["recv"][kept])), r
+        if e["scales"] is not None:
+            assert torch.equal(b(go["scales"][kept]), b(e["scales"][kept])), r
+        if e["out"] is not None:
+            assert torch.equal(b(go["out"]), b(e["out"])), r
