@@ -1,5 +1,5 @@
 // A plain C++ host program that uses libep only through include/ep.h:
-// hipMalloc'd buffers, the five entry points on the null stream, hipMemcpy
+// hipMalloc'd buffers, the six entry points on the null stream, hipMemcpy
 // back.  It checks properties that hold at any size, without the oracle:
 //   token choice ("DeepEP-Ascend" README, API Overview): counts sum to the
 //   valid (t,k); offsets are their exclusive prefix; slots are a bijection
@@ -10,7 +10,9 @@
 //   expert choice ("[Feature Request] Support Expert-Choice Routing via
 //   Native Expert-Centric API", Solution 1): the inverse map lists each
 //   token's entries in ascending order, received rows equal their tokens'
-//   rows, and the unit-weight combine gives bf16(picks_t * x_t).
+//   rows, and the unit-weight combine gives bf16(picks_t * x_t);
+//   the one-launch low-latency dispatch: expert e's rows in ascending (t,k)
+//   from e*cap, capacity overflow dropped and counted, recv_count.
 // Exit status 0 = every check passed.  Built by tests/capi/build.py.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -231,6 +233,87 @@ static int expert_choice()
     return 0;
 }
 
+// The one-launch low-latency dispatch into [E, cap] rows with overflow:
+// expert e's rows are e*cap + 0, 1, ... in ascending (t,k), entries beyond
+// cap get -1; recv_count, num_dropped and num_invalid follow from the
+// per-expert counts; rows equal their sources and the unit-weight combine
+// over the padded rows gives bf16(m_t * x_t).
+static int low_latency()
+{
+    const int T = 128, H = 512, E = 32, K = 6, cap = 12;
+    const int TK = T * K, rows = E * cap;
+    std::vector<int32_t> idx(TK);
+    for (auto &v : idx) {
+        const uint32_t u = rnd() % 100;
+        v = u < 10 ? -1 : (int32_t)(u < 30 ? rnd() % 3 : rnd() % E);   // padding; hot experts
+    }
+    std::vector<uint16_t> x((size_t)T * H);
+    for (auto &v : x)
+        v = (uint16_t)(((rnd() & 1u) << 15) | ((uint32_t)(110 + rnd() % 30) << 7) | (rnd() & 0x7Fu));
+    int32_t *d_idx, *d_slot, *d_src, *d_cnt, *d_nd, *d_ninv;
+    uint16_t *d_x, *d_recv, *d_out;
+    HIP_OK(hipMalloc(&d_idx, TK * 4));
+    HIP_OK(hipMalloc(&d_slot, TK * 4));
+    HIP_OK(hipMalloc(&d_src, rows * 4));
+    HIP_OK(hipMalloc(&d_cnt, E * 4));
+    HIP_OK(hipMalloc(&d_nd, 4));
+    HIP_OK(hipMalloc(&d_ninv, 4));
+    HIP_OK(hipMalloc(&d_x, (size_t)T * H * 2));
+    HIP_OK(hipMalloc(&d_recv, (size_t)rows * H * 2));
+    HIP_OK(hipMalloc(&d_out, (size_t)T * H * 2));
+    HIP_OK(hipMemcpy(d_idx, idx.data(), TK * 4, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(d_x, x.data(), (size_t)T * H * 2, hipMemcpyHostToDevice));
+
+    EP_OK_(ep_low_latency_dispatch(d_x, T, H, d_idx, K, E, cap, EP_QUANT_BF16, d_recv, nullptr,
+                                   d_slot, d_src, d_cnt, d_nd, d_ninv, nullptr));
+    EP_OK_(ep_combine(d_recv, rows, H, d_slot, nullptr, T, K, d_out, nullptr));
+    HIP_OK(hipDeviceSynchronize());
+
+    std::vector<int32_t> slot(TK), src(rows), cnt(E);
+    std::vector<uint16_t> recv((size_t)rows * H), out((size_t)T * H);
+    int32_t nd, ninv;
+    HIP_OK(hipMemcpy(slot.data(), d_slot, TK * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(src.data(), d_src, rows * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(cnt.data(), d_cnt, E * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(recv.data(), d_recv, (size_t)rows * H * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(out.data(), d_out, (size_t)T * H * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(&nd, d_nd, 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(&ninv, d_ninv, 4, hipMemcpyDeviceToHost));
+
+    std::vector<int> next(E, 0), m(T, 0);
+    for (int t = 0; t < T; ++t)
+        for (int k = 0; k < K; ++k) {
+            const int e = idx[t * K + k], s = slot[t * K + k];
+            if (e < 0) {
+                expect(s == -1, "ll: padding gets no slot", t);
+                continue;
+            }
+            const int r = next[e]++;
+            expect(s == (r < cap ? e * cap + r : -1), "ll: expert rows in ascending (t,k)", s);
+            if (s < 0)
+                continue;
+            expect(src[s] == t, "ll: recv_src is the source token", s);
+            expect(memcmp(&recv[(size_t)s * H], &x[(size_t)t * H], (size_t)H * 2) == 0,
+                   "ll: received row equals its source row", s);
+            ++m[t];
+        }
+    int dropped = 0;
+    for (int e = 0; e < E; ++e) {
+        expect(cnt[e] == (next[e] < cap ? next[e] : cap), "ll: recv_count = min(count, cap)", e);
+        dropped += next[e] > cap ? next[e] - cap : 0;
+    }
+    expect(dropped > 0 && nd == dropped, "ll: num_dropped", nd);
+    expect(ninv == 0, "ll: no invalid entry", ninv);
+    for (int t = 0; t < T; ++t)
+        for (int h = 0; h < H; ++h) {
+            const float p = (float)m[t] * bf16_value(x[(size_t)t * H + h]);
+            expect(out[(size_t)t * H + h] == bf16_nearest(p), "ll: unit-weight combine", t);
+        }
+    hipFree(d_idx); hipFree(d_slot); hipFree(d_src); hipFree(d_cnt); hipFree(d_nd);
+    hipFree(d_ninv); hipFree(d_x); hipFree(d_recv); hipFree(d_out);
+    return 0;
+}
+
 int main()
 {
     int dev_count = 0;
@@ -239,7 +322,7 @@ int main()
         fprintf(stderr, "no GPU\n");
         return 2;
     }
-    if (token_choice() || expert_choice())
+    if (token_choice() || low_latency() || expert_choice())
         return 2;
     if (failures) {
         fprintf(stderr, "%d check(s) failed\n", failures);
