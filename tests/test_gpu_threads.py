@@ -1,8 +1,9 @@
 """Concurrent calls from several host threads, each on its own stream.
 
 The library keeps no state between calls, so calls on different streams may
-overlap.  Four threads, each with its own stream, workspace and shape (bf16
-contiguous, fp8 into a padded buffer, MXFP4, expert choice), run the whole
+overlap.  Five threads, each with its own stream, buffers and shape (bf16
+contiguous, fp8 into a padded buffer, MXFP4, the one-launch low-latency
+dispatch with its combine, expert choice), run the whole
 path several times at once; every result must equal, bit for bit, the same
 calls made one after another on the default stream.  ctypes releases the
 interpreter lock during each library call, so the host-side code (argument
@@ -42,6 +43,21 @@ def _tc_job(seed, T, H, E, K, quant, recv_layout, cap):
     return run
 
 
+def _ll_job(seed, T, H, E, K, cap):
+    c = W.random_token_choice(seed, T, H, E, K, p_pad=0.1, p_invalid=0.02, p_dup=0.1)
+    x = torch.from_numpy(c.x.view(np.int16)).cuda().view(torch.bfloat16)
+    idx = torch.from_numpy(c.topk_idx).cuda()
+    w = torch.from_numpy(c.topk_weights).cuda()
+
+    def run():
+        recv, scales, h = api.low_latency_dispatch(x, idx, cap, E, quant="bf16")
+        out = api.low_latency_combine(recv, idx, w, h)
+        kept = h.slot[h.slot >= 0].long()
+        return [h.slot, h.recv_count, h.num_dropped, h.num_invalid,
+                recv.reshape(E * cap, H)[kept].view(torch.int16), out.view(torch.int16)]
+    return run
+
+
 def _ec_job(seed):
     c = W.random_expert_choice(seed, 900, 512, 16, 48, p_empty=0.1, hot=5)
     x = torch.from_numpy(c.x.view(np.int16)).cuda().view(torch.bfloat16)
@@ -62,6 +78,7 @@ def test_concurrent_streams_match_sequential_calls():
     jobs = [_tc_job(11, 1500, 2048, 64, 8, "bf16", "contiguous", None),
             _tc_job(12, 700, 1024, 32, 6, "fp8_e4m3_g128", "padded", 40),
             _tc_job(13, 1200, 768, 48, 4, "mxfp4_e2m1", "contiguous", None),
+            _ll_job(15, 256, 1024, 64, 8, 20),
             _ec_job(14)]
     torch.cuda.synchronize()
     expected = []
