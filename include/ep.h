@@ -197,9 +197,9 @@ ep_status_t ep_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx
  * Each block ranks its own token's entries by counting equal experts among
  * the entries before them, so the work grows as (T*K)^2: built for decode
  * batches.  Limits (EP_ERR_UNSUPPORTED beyond them; the layout + dispatch
- * pair has none of them): T*K <= 4096, K <= 64, and for the per-token modes
- * a row of at most 512 units of 16 channels (H <= 8192 when H/8 is even,
- * else H <= 4096).  Other constraints as ep_dispatch, with 1 <= E <= 4096,
+ * pair has none of these): T*K <= 4096, K <= 64, and for the per-token
+ * modes a row that one block holds (H <= 8192 when H/8 is even, else
+ * H <= 4096).  Other constraints as ep_dispatch, with 1 <= E <= 4096,
  * cap >= 0 and E*cap < 2^31.
  */
 ep_status_t ep_low_latency_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx,
