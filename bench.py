@@ -20,9 +20,11 @@ on, in a second pass after the timed region), a cold-cache pass (1 GiB of
 scratch read before each step, outside its events, so that neither L2 nor
 the 256 MB MALL holds the inputs), the roofline of the dominant
 kernel (algorithmic bytes per launch over its average duration, against
-8 TB/s), HBM traffic from the committed rocprofv3 counter summary when it was
-taken on the current kernel sources, and the CPU oracle timed on the host on
-a bounded sample of the same workload.
+8 TB/s), memory traffic from the committed rocprofv3 counter summary when it
+was taken on the current kernel sources, and the CPU leg: the outputs of the
+last timed step checked against the CPU oracle ("parity"; the run exits 1
+on a mismatch), then the oracle timed on a bounded sample of the same
+workload, on one host thread and, built with -fopenmp, on all host cores.
 """
 import argparse
 import hashlib
@@ -75,29 +77,60 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def traffic_entry(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    or None when that summary was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def _profile(kind, key):
+    """A committed profile summary (profiles/<kind>_<key>.json), or None when
+    it is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{key}.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("src_sha256") != kernel_source_hash():
-        return None
-    k = t.get("kernels", {}).get(kernel)
+    return t if t.get("src_sha256") == kernel_source_hash() else None
+
+
+def traffic_entry(key, kernel):
+    """Bytes per launch of `kernel` between L2 and memory (rocprofv3
+    FETCH_SIZE + WRITE_SIZE, calibrated), from the committed counter summary
+    taken on the current kernel sources; else None."""
+    t = _profile("traffic", key)
+    k = None if t is None else t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def trace_avg_us(key, kernel):
+    """Average duration of `kernel` in the committed rocprofv3 kernel trace of
+    the same command, taken on the current kernel sources; else None."""
+    t = _profile("kernels", key)
+    k = None if t is None else t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("avg_us")
+
+
+def workload_key(c, meta, chunk, two_call):
+    """Name of a bench configuration: the workload, plus the dispatch mode
+    when it is not the workload's own, the round size and the decode form."""
+    key = c.name
+    if meta.get("quant") is not None and meta["quant"] != getattr(c, "default_quant", None):
+        key += "_" + meta["quant"]
+    if chunk:
+        key += f"_chunk{chunk}"
+    if two_call:
+        key += "_two_call"
+    return key
 
 
 # ----------------------------------------------------------------- paths
 class Path:
     """A workload's hot path: named operations (each a list of libep calls on
-    one stream), the main kernel of each, and algorithmic bytes per op."""
+    one stream), the main kernel of each, algorithmic bytes per op, and the
+    device buffers the step writes (checked against the oracle after the
+    timed region)."""
 
-    def __init__(self, name, T, ops, kernel_of, alg_bytes, meta):
+    def __init__(self, name, T, ops, kernel_of, alg_bytes, meta, kind="token_choice",
+                 outputs=None):
         self.name, self.T, self.ops, self.kernel_of = name, T, ops, kernel_of
         self.alg_bytes, self.meta = alg_bytes, meta
+        self.kind, self.outputs = kind, outputs or {}
 
 
 # quant name -> (ep_quant_t attribute, bytes of a receive row, scale shape)
@@ -193,7 +226,9 @@ def chunked_token_choice_path(c, N, torch, dev, sp, chunk):
     meta = {"T": T, "H": H, "E": E, "top_k": K, "recv_layout": "contiguous", "quant": "bf16",
             "combine": "weighted", "valid_slots": n_valid, "chunk_tokens": chunk,
             "rounds": (T + chunk - 1) // chunk, "receive_rows": rows}
-    return Path(c.name, T, ops, kern, alg, meta)
+    last = (T - 1) // chunk * chunk
+    return Path(c.name, T, ops, kern, alg, meta, kind="chunked",
+                outputs={"out": out, "slot": slot[:T - last], "last_round_t0": last})
 
 
 def token_choice_path(c, N, torch, dev, sp):
@@ -260,7 +295,10 @@ def token_choice_path(c, N, torch, dev, sp):
     meta = {"T": T, "H": H, "E": E, "top_k": K, "recv_layout": c.layout, "quant": quant,
             "cap": c.cap, "combine": "weighted", "valid_slots": n_valid}
     return Path(c.name, T, [("layout", layout), ("dispatch", dispatch), ("combine", combine)],
-                kern, alg, meta)
+                kern, alg, meta,
+                outputs={"counts": counts, "offsets": offsets, "num_invalid": ninv,
+                         "slot": slot, "recv_src": src, "num_dropped": nd, "recv": recv,
+                         "scales": scales, "out": out})
 
 
 def low_latency_path(c, N, torch, dev, sp):
@@ -315,7 +353,10 @@ def low_latency_path(c, N, torch, dev, sp):
     meta = {"T": T, "H": H, "E": E, "top_k": K, "recv_layout": "padded", "quant": quant,
             "cap": cap, "combine": "weighted", "valid_slots": n_valid,
             "dispatch": "ep_low_latency_dispatch (one launch)"}
-    return Path(c.name, T, [("dispatch", dispatch), ("combine", combine)], kern, alg, meta)
+    return Path(c.name, T, [("dispatch", dispatch), ("combine", combine)], kern, alg, meta,
+                outputs={"slot": slot, "recv_src": src, "num_dropped": nd, "recv": recv,
+                         "scales": scales, "recv_count": cnt, "num_invalid": ninv,
+                         "out": out})
 
 
 def expert_choice_path(c, N, torch, dev, sp):
@@ -347,47 +388,187 @@ def expert_choice_path(c, N, torch, dev, sp):
     kern = {"dispatch": "ec_dispatch_fused_kernel", "combine": "ec_combine_kernel"}
     meta = {"T": T, "H": H, "E": E, "capacity": C, "valid_entries": n_valid,
             "distinct_tokens": U}
-    return Path(c.name, T, [("dispatch", dispatch), ("combine", combine)], kern, alg, meta)
+    return Path(c.name, T, [("dispatch", dispatch), ("combine", combine)], kern, alg, meta,
+                kind="expert_choice",
+                outputs={"recv": recv, "tok_off": off, "tok_ent": ent, "num_invalid": ninv,
+                         "out": out})
 
 
-def cpu_baseline(c, budget_s):
-    """The oracle as it stands (single thread) on full passes of the same
-    workload until `budget_s` seconds have elapsed."""
-    import oracle
+def snapshot(path, torch):
+    """Host copies of the buffers the last timed step wrote (bf16 as bit
+    patterns), taken right after the timed region."""
+    g = {}
+    for k, t in path.outputs.items():
+        if t is None:
+            continue
+        if not hasattr(t, "dtype"):
+            g[k] = t
+        elif t.dtype == torch.bfloat16:
+            g[k] = t.view(torch.int16).cpu().numpy().view(np.uint16)
+        else:
+            g[k] = t.cpu().numpy()
+    return g
+
+
+def _combine_bad(got_bits, ref_bits):
+    """Elements outside |gpu - oracle| <= 2^-7 |oracle| + 1e-3 (fp32-widened
+    bf16); a NaN or infinity on either side counts as outside."""
+    f = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32) \
+        .astype(np.float64)
+    g, r = f(got_bits), f(ref_bits)
+    with np.errstate(invalid="ignore", over="ignore"):
+        return int(np.count_nonzero(~(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-3)))
+
+
+class _Checks:
+    def __init__(self):
+        self.done, self.failed = [], []
+
+    def equal(self, name, got, want):
+        ok = got.shape == want.shape and np.array_equal(
+            np.ascontiguousarray(got).view(np.uint8), np.ascontiguousarray(want).view(np.uint8))
+        (self.done if ok else self.failed).append(name)
+
+    def close(self, name, got, want):
+        bad = _combine_bad(got, want) if got.shape == want.shape else -1
+        (self.done if bad == 0 else self.failed).append(name if bad == 0 else f"{name} ({bad})")
+
+
+def _oracle_quant_rows(oracle, c, slot, rows, quant):
+    if quant == "fp8_e4m3_g128":
+        return oracle.dispatch_fp8(c.x, slot, rows)
+    if quant in oracle.TOKEN_FMT:
+        return oracle.dispatch_token_quant(c.x, slot, rows, quant)
+    return oracle.dispatch_mx(c.x, slot, rows, quant)
+
+
+def _check_token_choice(oracle, torch, c, path, g, ck):
+    meta = path.meta
+    T, H, E, K = c.T, c.H, c.E, c.K
+    padded = meta["recv_layout"] == "padded"
+    cap = c.cap if padded else T * K
+    rows = E * cap if padded else T * K
+    quant = meta["quant"]
+    ref = oracle.layout(c.topk_idx, E)
+    if "offsets" in g:
+        ck.equal("counts", g["counts"], ref["counts"])
+        ck.equal("offsets", g["offsets"], ref["offsets"])
+        ck.equal("num_invalid", g["num_invalid"], np.array([ref["num_invalid"]], np.int32))
+    if "recv_count" in g:
+        ck.equal("recv_count", g["recv_count"], np.minimum(ref["counts"], cap).astype(np.int32))
+        ck.equal("num_invalid", g["num_invalid"], np.array([ref["num_invalid"]], np.int32))
+    s_ref, src_ref, nd_ref = oracle.slots(c.topk_idx, E, padded, cap)
+    ck.equal("slot", g["slot"], s_ref)
+    ck.equal("num_dropped", g["num_dropped"], np.array([nd_ref], np.int32))
+    wr = s_ref[s_ref >= 0]
+    ck.equal("recv_src", g["recv_src"][wr], src_ref[wr])
+    if quant == "bf16":
+        y = oracle.dispatch_bf16(c.x, s_ref, rows)
+        ck.equal("recv rows", g["recv"][wr], y[wr])
+    else:
+        q_ref, sc_ref = _oracle_quant_rows(oracle, c, s_ref, rows, quant)
+        ck.equal("recv codes", g["recv"][wr], q_ref[wr])
+        ck.equal("recv scales", g["scales"][wr], sc_ref[wr])
+        # the identity expert's input: the oracle's codes dequantised by the
+        # same torch casts (on the CPU) that made the GPU's y
+        yq = dequantise(torch, torch.from_numpy(q_ref), torch.from_numpy(sc_ref), quant, H)
+        y = yq.view(torch.int16).numpy().view(np.uint16)
+    ck.close("combine", g["out"], oracle.combine(y, s_ref, c.topk_weights))
+    return f"{quant} {'padded' if padded else 'contiguous'}: " \
+           f"{len(wr)} receive rows, {T} combined tokens"
+
+
+def _check_chunked(oracle, c, path, g, ck):
+    T, K, E = c.T, c.K, c.E
+    t0 = g["last_round_t0"]
+    s_last, _, _ = oracle.slots(c.topk_idx[t0:], E, False, (T - t0) * K)
+    ck.equal("slot (last round)", g["slot"], s_last)
+    s_ref, _, _ = oracle.slots(c.topk_idx, E, False, T * K)
+    y = oracle.dispatch_bf16(c.x, s_ref, T * K)
+    ck.close("combine", g["out"], oracle.combine(y, s_ref, c.topk_weights))
+    return f"chunked: last round's slots, {T} combined tokens against the unchunked oracle"
+
+
+def _check_expert_choice(oracle, c, path, g, ck):
+    recv, ninv = oracle.ec_dispatch(c.x, c.token_indices)
+    off, ent = oracle.ec_invert(c.token_indices, c.T)
+    ck.equal("tok_off", g["tok_off"], off)
+    n = int(off[-1])
+    ck.equal("tok_ent", g["tok_ent"][:n], ent[:n])
+    ck.equal("num_invalid", g["num_invalid"], np.array([ninv], np.int32))
+    flat = c.token_indices.reshape(-1)
+    keep = (flat >= 0) & (flat < c.T)
+    gr = g["recv"].reshape(-1, c.H)
+    ck.equal("recv rows", gr[keep], recv.reshape(-1, c.H)[keep])
+    ck.close("combine", g["out"], oracle.ec_combine(recv, c.weights, c.token_indices, c.T))
+    return f"expert choice: {int(keep.sum())} receive rows, inverse map, {c.T} combined tokens"
+
+
+def _oracle_pass(oracle, c):
+    """One full pass of the workload through the oracle."""
+    if hasattr(c, "token_indices"):
+        recv, _ = oracle.ec_dispatch(c.x, c.token_indices)
+        oracle.ec_invert(c.token_indices, c.T)
+        oracle.ec_combine(recv, c.weights, c.token_indices, c.T)
+        return "expert-choice dispatch, inverse map, weighted combine"
+    padded = c.layout == "padded"
+    cap = c.cap if padded else c.T * c.K
+    rows = c.E * c.cap if padded else c.T * c.K
+    oracle.layout(c.topk_idx, c.E)
+    slot, _, _ = oracle.slots(c.topk_idx, c.E, padded, cap)
+    if c.quant == "bf16":
+        y = oracle.dispatch_bf16(c.x, slot, rows)
+    else:
+        _oracle_quant_rows(oracle, c, slot, rows, c.quant)
+        y = np.zeros((rows, c.H), np.uint16)
+    oracle.combine(y, slot, c.topk_weights)
+    return "layout, slots, dispatch, weighted combine"
+
+
+def _time_oracle(oracle, c, budget_s):
     reps = 0
     t0 = time.perf_counter()
     while True:
-        if hasattr(c, "token_indices"):
-            recv, _ = oracle.ec_dispatch(c.x, c.token_indices)
-            oracle.ec_invert(c.token_indices, c.T)
-            oracle.ec_combine(recv, c.weights, c.token_indices, c.T)
-            what = "expert-choice dispatch, inverse map, weighted combine"
-        else:
-            padded = c.layout == "padded"
-            cap = c.cap if padded else c.T * c.K
-            rows = c.E * c.cap if padded else c.T * c.K
-            oracle.layout(c.topk_idx, c.E)
-            slot, _, _ = oracle.slots(c.topk_idx, c.E, padded, cap)
-            if c.quant == "bf16":
-                y = oracle.dispatch_bf16(c.x, slot, rows)
-            else:
-                if c.quant == "fp8_e4m3_g128":
-                    oracle.dispatch_fp8(c.x, slot, rows)
-                elif c.quant in oracle.TOKEN_FMT:
-                    oracle.dispatch_token_quant(c.x, slot, rows, c.quant)
-                else:
-                    oracle.dispatch_mx(c.x, slot, rows, c.quant)
-                y = np.zeros((rows, c.H), np.uint16)
-            oracle.combine(y, slot, c.topk_weights)
-            what = "layout, slots, dispatch, weighted combine"
+        what = _oracle_pass(oracle, c)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
-            break
-    return {"value": reps * c.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            return reps, el, what
+
+
+def cpu_baseline(c, path, g, budget_s, torch):
+    """The CPU leg.  (1) Parity: the oracle on the same inputs, compared
+    with the outputs of the last timed GPU step (`g`): bit for bit for the
+    layout, slots, counters, receive rows, codes and scales, the combine
+    within 2^-7 |oracle| + 1e-3.  (2) The oracle as it stands, timed on full
+    passes of the same workload for `budget_s` seconds: the plain build on
+    one host thread, then the same source built with -fopenmp on all host
+    cores.  Returns (parity, cpu_baseline, cpu_baseline_all_cores)."""
+    import oracle
+    ck = _Checks()
+    if path.kind == "expert_choice":
+        what = _check_expert_choice(oracle, c, path, g, ck)
+    elif path.kind == "chunked":
+        what = _check_chunked(oracle, c, path, g, ck)
+    else:
+        what = _check_token_choice(oracle, torch, c, path, g, ck)
+    parity = {"status": "fail" if ck.failed else "ok", "checked": what,
+              "outputs": ck.done, "failed": ck.failed}
+    if budget_s <= 0:
+        return parity, None, None
+    host = {"host_cpu": host_cpu_model(), "host_logical_cpus": os.cpu_count()}
+    reps, el, what = _time_oracle(oracle, c, budget_s)
+    one = {"value": reps * c.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+           "sample": f"{reps} full pass(es) of the same workload ({what}; {c.T} tokens each), "
+                     f"{el:.1f} s on one host thread", **host}
+    with oracle.all_cores() as threads:
+        reps, el, what = _time_oracle(oracle, c, budget_s)
+    allc = {"value": reps * c.T / el, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle (-fopenmp build: token-major loops parallel, layout and slots "
+                    "serial)",
             "sample": f"{reps} full pass(es) of the same workload ({what}; {c.T} tokens each), "
-                      f"{el:.1f} s on one host thread",
-            "host_cpu": host_cpu_model(), "host_logical_cpus": os.cpu_count()}
+                      f"{el:.1f} s on {threads} threads", **host}
+    return parity, one, allc
 
 
 def host_cpu_model():
@@ -432,6 +613,9 @@ def main():
                          "outside the step's events (0 = no cold pass)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
+    ap.add_argument("--no-check", action="store_true",
+                    help="with --cpu-budget 0: skip the check of the timed outputs against "
+                         "the oracle (profiling runs)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the multi-GPU "
@@ -447,6 +631,7 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     c = W.WORKLOADS[a.workload]()
+    c.default_quant = getattr(c, "quant", None)
     if a.quant is not None:
         if a.workload == "expert_choice":
             print("--quant applies to token-choice workloads only", file=sys.stderr)
@@ -489,6 +674,9 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / a.steps
     region_ms = r0.elapsed_time(r1) / a.steps
+    # the outputs of the last timed step, checked against the oracle at the end
+    check = a.cpu_budget > 0 or not a.no_check
+    g = snapshot(path, torch) if check else None
 
     # per-operation durations: a second pass of K steps with HIP events
     # around each operation on the stream the kernels run on
@@ -540,6 +728,7 @@ def main():
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     headline = (a.workload == "prefill" and path.meta.get("quant") == "bf16"
                 and "chunk_tokens" not in path.meta)
+    key = workload_key(c, path.meta, a.chunk, a.two_call and a.workload == "decode")
     res = {
         "metric": HEADLINE_METRIC if headline else
                   f"dispatch+combine tokens/s & achieved HBM GB/s, {c.name}"
@@ -570,14 +759,30 @@ def main():
         "roofline": {"bound": "hbm", "kernel": path.kernel_of[dom], "op": dom,
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": traffic_entry(a.workload, path.kernel_of[dom]),
-                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": dom_us},
+                     "traffic": traffic_entry(key, path.kernel_of[dom]),
+                     "traffic_kind": "bytes between L2 and memory per launch (rocprofv3 "
+                                     "FETCH_SIZE + WRITE_SIZE scaled by a 1 GiB copy kernel's "
+                                     "readings; L2 misses, so MALL hits count too), from "
+                                     f"profiles/traffic_{key}.json when it was taken on the "
+                                     "current kernel sources, else null",
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": dom_us,
+                     "avg_launch_us_source": "HIP events around each launch on the kernels' "
+                                             "stream, second pass of K steps (includes the "
+                                             "event packets' gaps)",
+                     "rocprof_avg_us": trace_avg_us(key, path.kernel_of[dom])},
     }
     res["cold"] = cold
     res["inputs_sha256"] = inputs_sha256(c)
-    if a.cpu_budget > 0:
-        res["cpu_baseline"] = cpu_baseline(c, a.cpu_budget)
+    parity = None
+    if check:
+        parity, one, allc = cpu_baseline(c, path, g, a.cpu_budget, torch)
+        if one is not None:
+            res["cpu_baseline"] = one
+            res["cpu_baseline_all_cores"] = allc
+    res["parity"] = parity
     print(json.dumps(res), flush=True)
+    if parity is not None and parity["status"] != "ok":
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -7,6 +7,7 @@ arguments; all arithmetic is in oracle.c.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -16,18 +17,25 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# the same source built with -fopenmp: the all-host-cores CPU baseline
+_LIB_OMP = os.path.join(_HERE, "liboracle_omp.so")
 _CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
 _lib = None
+_lib_omp = None
+_override = None
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc into oracle/liboracle.so."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, openmp: bool = False) -> str:
+    """Compile oracle.c with gcc into oracle/liboracle.so (or, with openmp,
+    the parallel build oracle/liboracle_omp.so)."""
+    out = _LIB_OMP if openmp else _LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        extra = ["-fopenmp"] if openmp else []
+        subprocess.run(["gcc", *_CFLAGS, *extra, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
 
 
 _P = ctypes.c_void_p
@@ -37,6 +45,8 @@ _I64 = ctypes.c_int64
 
 def lib():
     global _lib
+    if _override is not None:
+        return _override
     if _lib is None:
         # ORACLE_LIB names another build of oracle.c: the mutation test loads
         # deliberately broken copies this way to show that the pins catch them
@@ -45,43 +55,66 @@ def lib():
             path = _LIB
             if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
                 build()
-        L = ctypes.CDLL(path)
-        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
-        L.oracle_bf16_to_f32.restype = ctypes.c_float
-        L.oracle_bf16_from_f64.argtypes = [ctypes.c_double]
-        L.oracle_bf16_from_f64.restype = ctypes.c_uint16
-        L.oracle_e4m3_from_f32.argtypes = [ctypes.c_float]
-        L.oracle_e4m3_from_f32.restype = ctypes.c_uint8
-        L.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
-        L.oracle_e4m3_to_f32.restype = ctypes.c_float
-        L.oracle_e4m3_from_f32_array.argtypes = [_P, _P, _I64]
-        L.oracle_e5m2_from_f32_array.argtypes = [_P, _P, _I64]
-        L.oracle_e2m1_from_f32_array.argtypes = [_P, _P, _I64]
-        L.oracle_e5m2_to_f32.argtypes = [ctypes.c_uint8]
-        L.oracle_e5m2_to_f32.restype = ctypes.c_float
-        L.oracle_e2m1_to_f32.argtypes = [ctypes.c_uint8]
-        L.oracle_e2m1_to_f32.restype = ctypes.c_float
-        L.oracle_int8_from_f32.argtypes = [ctypes.c_float]
-        L.oracle_int8_from_f32.restype = ctypes.c_int8
-        L.oracle_dispatch_token_quant.argtypes = [_P, _I, _I, _P, _I, _I, _P, _P]
-        L.oracle_dispatch_mx.argtypes = [_P, _I, _I, _P, _I, _I, _P, _P]
-        L.oracle_bf16_from_f64_array.argtypes = [_P, _P, _I64]
-        L.oracle_layout.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P]
-        L.oracle_slots.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _P]
-        L.oracle_dispatch_bf16.argtypes = [_P, _I, _I, _P, _I, _P]
-        L.oracle_dispatch_fp8.argtypes = [_P, _I, _I, _P, _I, _P, _P]
-        L.oracle_combine.argtypes = [_P, _I, _P, _P, _I, _I, _P]
-        L.oracle_ec_dispatch.argtypes = [_P, _I, _I, _P, _I, _I, _P, _P]
-        L.oracle_ec_invert.argtypes = [_P, _I, _I, _I, _P, _P]
-        L.oracle_ec_combine.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P]
-        for f in ("oracle_layout", "oracle_slots", "oracle_dispatch_bf16", "oracle_dispatch_fp8",
-                  "oracle_combine", "oracle_ec_dispatch", "oracle_ec_invert", "oracle_ec_combine",
-                  "oracle_e4m3_from_f32_array", "oracle_bf16_from_f64_array",
-                  "oracle_e5m2_from_f32_array", "oracle_e2m1_from_f32_array",
-                  "oracle_dispatch_token_quant", "oracle_dispatch_mx"):
-            getattr(L, f).restype = None
-        _lib = L
+        _lib = _load(path)
     return _lib
+
+
+@contextlib.contextmanager
+def all_cores():
+    """Within the block, every oracle call runs on the -fopenmp build of the
+    same source (its token-major loops in parallel over all host cores).
+    Yields the number of threads it uses."""
+    global _lib_omp, _override
+    if _lib_omp is None:
+        if not os.path.exists(_LIB_OMP) or os.path.getmtime(_LIB_OMP) < os.path.getmtime(_SRC):
+            build(openmp=True)
+        _lib_omp = _load(_LIB_OMP)
+    prev, _override = _override, _lib_omp
+    try:
+        yield int(_lib_omp.oracle_max_threads())
+    finally:
+        _override = prev
+
+
+def _load(path):
+    L = ctypes.CDLL(path)
+    L.oracle_max_threads.argtypes = []
+    L.oracle_max_threads.restype = ctypes.c_int
+    L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    L.oracle_bf16_to_f32.restype = ctypes.c_float
+    L.oracle_bf16_from_f64.argtypes = [ctypes.c_double]
+    L.oracle_bf16_from_f64.restype = ctypes.c_uint16
+    L.oracle_e4m3_from_f32.argtypes = [ctypes.c_float]
+    L.oracle_e4m3_from_f32.restype = ctypes.c_uint8
+    L.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+    L.oracle_e4m3_to_f32.restype = ctypes.c_float
+    L.oracle_e4m3_from_f32_array.argtypes = [_P, _P, _I64]
+    L.oracle_e5m2_from_f32_array.argtypes = [_P, _P, _I64]
+    L.oracle_e2m1_from_f32_array.argtypes = [_P, _P, _I64]
+    L.oracle_e5m2_to_f32.argtypes = [ctypes.c_uint8]
+    L.oracle_e5m2_to_f32.restype = ctypes.c_float
+    L.oracle_e2m1_to_f32.argtypes = [ctypes.c_uint8]
+    L.oracle_e2m1_to_f32.restype = ctypes.c_float
+    L.oracle_int8_from_f32.argtypes = [ctypes.c_float]
+    L.oracle_int8_from_f32.restype = ctypes.c_int8
+    L.oracle_dispatch_token_quant.argtypes = [_P, _I, _I, _P, _I, _I, _P, _P]
+    L.oracle_dispatch_mx.argtypes = [_P, _I, _I, _P, _I, _I, _P, _P]
+    L.oracle_bf16_from_f64_array.argtypes = [_P, _P, _I64]
+    L.oracle_layout.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P]
+    L.oracle_slots.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _P]
+    L.oracle_dispatch_bf16.argtypes = [_P, _I, _I, _P, _I, _P]
+    L.oracle_dispatch_fp8.argtypes = [_P, _I, _I, _P, _I, _P, _P]
+    L.oracle_combine.argtypes = [_P, _I, _P, _P, _I, _I, _P]
+    L.oracle_ec_dispatch.argtypes = [_P, _I, _I, _P, _I, _I, _P, _P]
+    L.oracle_ec_invert.argtypes = [_P, _I, _I, _I, _P, _P]
+    L.oracle_ec_combine.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P]
+    for f in ("oracle_layout", "oracle_slots", "oracle_dispatch_bf16", "oracle_dispatch_fp8",
+              "oracle_combine", "oracle_ec_dispatch", "oracle_ec_invert", "oracle_ec_combine",
+              "oracle_e4m3_from_f32_array", "oracle_bf16_from_f64_array",
+              "oracle_e5m2_from_f32_array", "oracle_e2m1_from_f32_array",
+              "oracle_dispatch_token_quant", "oracle_dispatch_mx"):
+        getattr(L, f).restype = None
+    return L
 
 
 def _c(a, dtype):

@@ -23,7 +23,15 @@
  * accumulation precision), the reading taken is stated at the function.
  *
  * Floating point: built with -O2 -ffp-contract=off, no fast-math, SSE
- * arithmetic (no excess precision).  fp32 is used exactly where the method
+ * arithmetic (no excess precision).
+ *
+ * Threads: the plain build is single-threaded.  The same source is built a
+ * second time with -fopenmp for the all-host-cores CPU baseline; then the
+ * token-major loops (the dispatch copies and their quantisation, the
+ * combines, the expert-choice copy) run their tokens or entries in
+ * parallel, each iteration writing its own rows, so the results are the
+ * same bytes.  Layout, slots and the inverse map stay serial (a running
+ * count), and the OpenMP pragmas are ignored by the plain build.  fp32 is used exactly where the method
  * fixes it (the fp8 scale and the value that is rounded to e4m3); sums are
  * accumulated in fp64 and rounded once.
  *
@@ -37,6 +45,19 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the parallel loops use (1 in the plain build). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------ */
 /* Number formats                                                      */
@@ -239,6 +260,7 @@ void oracle_slots(const int32_t *topk_idx, int T, int K, int E, int padded,
 void oracle_dispatch_bf16(const uint16_t *x, int T, int H, const int32_t *slot, int K,
                           uint16_t *recv)
 {
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t)
         for (int k = 0; k < K; ++k) {
             int32_t s = slot[(int64_t)t * K + k];
@@ -262,8 +284,11 @@ void oracle_dispatch_fp8(const uint16_t *x, int T, int H, const int32_t *slot, i
                          uint8_t *recv_q, float *recv_s)
 {
     int G = H / 128;
+#pragma omp parallel
+    {
     uint8_t *q = (uint8_t *)malloc((size_t)H + 1);
     float *s = (float *)malloc(((size_t)G + 1) * sizeof(float));
+#pragma omp for schedule(static)
     for (int t = 0; t < T; ++t) {
         const uint16_t *xr = x + (int64_t)t * H;
         for (int g = 0; g < G; ++g) {
@@ -296,6 +321,7 @@ void oracle_dispatch_fp8(const uint16_t *x, int T, int H, const int32_t *slot, i
     }
     free(q);
     free(s);
+    }
 }
 
 /* ------------------------------------------------------------------ */
@@ -412,8 +438,11 @@ void oracle_e2m1_from_f32_array(const float *in, uint8_t *out, int64_t n)
 void oracle_dispatch_token_quant(const uint16_t *x, int T, int H, const int32_t *slot, int K,
                                  int fmt, uint8_t *recv_q, float *recv_s)
 {
-    uint8_t *q = (uint8_t *)malloc((size_t)H + 1);
     const float Q = fmt == 1 ? 127.0f : 448.0f;
+#pragma omp parallel
+    {
+    uint8_t *q = (uint8_t *)malloc((size_t)H + 1);
+#pragma omp for schedule(static)
     for (int t = 0; t < T; ++t) {
         const uint16_t *xr = x + (int64_t)t * H;
         float a = 0.0f;
@@ -441,6 +470,7 @@ void oracle_dispatch_token_quant(const uint16_t *x, int T, int H, const int32_t 
         }
     }
     free(q);
+    }
 }
 
 /* MX dispatch (MXFP8 e4m3: fmt 0, MXFP8 e5m2: fmt 1, MXFP4 e2m1: fmt 2).
@@ -461,8 +491,11 @@ void oracle_dispatch_mx(const uint16_t *x, int T, int H, const int32_t *slot, in
     const int emax = emax_of[fmt];
     const int nb = H / 32;
     const int rb = fmt == 2 ? H / 2 : H;
+#pragma omp parallel
+    {
     uint8_t *q = (uint8_t *)malloc((size_t)rb + 1);
     uint8_t *ec = (uint8_t *)malloc((size_t)nb + 1);
+#pragma omp for schedule(static)
     for (int t = 0; t < T; ++t) {
         const uint16_t *xr = x + (int64_t)t * H;
         memset(q, 0, (size_t)rb);
@@ -505,6 +538,7 @@ void oracle_dispatch_mx(const uint16_t *x, int T, int H, const int32_t *slot, in
     }
     free(q);
     free(ec);
+    }
 }
 
 /* Combine ([EPA] API Overview: combine reduces the dispatched rows through
@@ -517,7 +551,10 @@ void oracle_dispatch_mx(const uint16_t *x, int T, int H, const int32_t *slot, in
 void oracle_combine(const uint16_t *y, int H, const int32_t *slot, const float *w,
                     int T, int K, uint16_t *out)
 {
+#pragma omp parallel
+    {
     double *acc = (double *)malloc(((size_t)H + 1) * sizeof(double));
+#pragma omp for schedule(static)
     for (int t = 0; t < T; ++t) {
         for (int h = 0; h < H; ++h)
             acc[h] = 0.0;
@@ -534,6 +571,7 @@ void oracle_combine(const uint16_t *y, int H, const int32_t *slot, const float *
             out[(int64_t)t * H + h] = oracle_bf16_from_f64(acc[h]);
     }
     free(acc);
+    }
 }
 
 /* ------------------------------------------------------------------ */
@@ -546,17 +584,19 @@ void oracle_combine(const uint16_t *y, int H, const int32_t *slot, const float *
 void oracle_ec_dispatch(const uint16_t *x, int T, int H, const int32_t *token_indices,
                         int E, int C, uint16_t *recv, int32_t *num_invalid)
 {
-    *num_invalid = 0;
+    int32_t inval = 0;
+#pragma omp parallel for schedule(static) reduction(+ : inval)
     for (int64_t j = 0; j < (int64_t)E * C; ++j) {
         int32_t i = token_indices[j];
         if (i == -1)
             continue;
         if (i < 0 || i >= T) {
-            (*num_invalid)++;
+            inval++;
             continue;
         }
         memcpy(recv + j * H, x + (int64_t)i * H, (size_t)H * sizeof(uint16_t));
     }
+    *num_invalid = inval;
 }
 
 /* Token -> entries map (the inverse of token_indices, kept as the handle for
@@ -595,7 +635,10 @@ void oracle_ec_combine(const uint16_t *y, const float *w, const int32_t *token_i
 {
     int64_t n = (int64_t)E * C;
     int count = tokens ? n_tokens : T;
+#pragma omp parallel
+    {
     double *acc = (double *)malloc(((size_t)H + 1) * sizeof(double));
+#pragma omp for schedule(static)
     for (int o = 0; o < count; ++o) {
         int t = tokens ? tokens[o] : o;
         for (int h = 0; h < H; ++h)
@@ -611,4 +654,5 @@ void oracle_ec_combine(const uint16_t *y, const float *w, const int32_t *token_i
             out[(int64_t)o * H + h] = oracle_bf16_from_f64(acc[h]);
     }
     free(acc);
+    }
 }

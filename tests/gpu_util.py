@@ -4,6 +4,7 @@ import numpy as np
 import torch
 
 import combine_get_dispatch_04_amd._native as N
+import tolerance as _tol
 
 DEV = "cuda"
 SENT16 = 0x7BAD      # sentinel bf16 pattern for rows nobody should write
@@ -120,16 +121,6 @@ def ec_combine(y_d, w_d, off_d, ent_d, T):
     return out
 
 
-def bf16_f64(bits: np.ndarray) -> np.ndarray:
-    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
-def assert_combine_close(got_bits, ref_bits, what=""):
-    """The combine tolerance: |gpu - oracle| <= 2^-7 |oracle| + 1e-3 per element."""
-    g = bf16_f64(got_bits)
-    r = bf16_f64(ref_bits)
-    err = np.abs(g - r)
-    lim = 2.0 ** -7 * np.abs(r) + 1e-3
-    bad = np.nonzero(err > lim)
-    assert bad[0].size == 0, (what, [(tuple(int(i) for i in ix), g[ix], r[ix])
-                                     for ix in list(zip(*bad))[:5]])
+# the combine tolerance (NaN-proof; see tests/tolerance.py)
+bf16_f64 = _tol.bf16_f64
+assert_combine_close = _tol.assert_combine_close

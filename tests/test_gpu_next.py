@@ -75,10 +75,9 @@ def test_expert_choice_workload_emulated():
     native = G.host(_native_ec(c))
     emu, _ = _emulated(tc)
     assert np.array_equal(native.view(np.uint16), G.host(emu).view(np.uint16))
-    toks = np.random.default_rng(5).choice(c.T, 256, replace=False)
     ref = oracle.ec_combine(oracle.ec_dispatch(c.x, c.token_indices)[0], c.weights,
-                            c.token_indices, c.T, tokens=toks.astype(np.int32))
-    G.assert_combine_close(native[toks], ref)
+                            c.token_indices, c.T)
+    G.assert_combine_close(native, ref)
 
 
 def _chunk_check(c, chunk, quant="bf16"):
@@ -125,9 +124,6 @@ def test_chunked_prefill():
     _announce("chunked prefill")
     c = W.prefill()
     out = _chunk_check(c, 1024)
-    toks = np.sort(np.random.default_rng(6).choice(c.T, 128, replace=False))
-    sub = c.topk_idx[toks]
-    s_ref, _, _ = oracle.slots(sub, c.E, False, toks.size * c.K)
-    ref = oracle.combine(oracle.dispatch_bf16(c.x[toks], s_ref, toks.size * c.K), s_ref,
-                         c.topk_weights[toks])
-    G.assert_combine_close(out[toks], ref)
+    s_ref, _, _ = oracle.slots(c.topk_idx, c.E, False, c.T * c.K)
+    ref = oracle.combine(oracle.dispatch_bf16(c.x, s_ref, c.T * c.K), s_ref, c.topk_weights)
+    G.assert_combine_close(out, ref)

@@ -98,7 +98,7 @@ MUTANTS = [
      "double wk = w ? (double)w[(int64_t)t * K + k] : 1.0;",
      "double wk = w ? (double)w[(int64_t)k * T + t] : 1.0;", TC),
     ("expert choice: invalid entries not counted",
-     "        if (i < 0 || i >= T) {\n            (*num_invalid)++;\n            continue;\n        }\n        memcpy(recv + j * H",
+     "        if (i < 0 || i >= T) {\n            inval++;\n            continue;\n        }\n        memcpy(recv + j * H",
      "        if (i < 0 || i >= T) {\n            continue;\n        }\n        memcpy(recv + j * H", EC),
     ("expert choice: a token's entries in descending order",
      "    for (int64_t j = 0; j < n; ++j) {\n        int32_t i = token_indices[j];\n        if (i >= 0 && i < T)\n            tok_ent[",
