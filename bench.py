@@ -66,43 +66,62 @@ def _code_only(text):
     return " ".join("".join(out).split())
 
 
-def kernel_source_hash():
-    """SHA-256 over the library sources (csrc/), comments and whitespace
-    excluded: the counter summaries in profiles/ are valid while it holds."""
+# The sources a kernel's code and launch shape come from (besides the
+# device helpers in ep_common.h).  A kernel not listed depends on all of csrc/.
+KERNEL_SOURCES = {
+    "layout_chunk_kernel": ["ep_layout.hip"],
+    "layout_scan_kernel": ["ep_layout.hip"],
+    "dispatch_kernel": ["ep_dispatch.hip", "ep_layout.hip"],
+    "combine_kernel": ["ep_combine.hip"],
+    "ec_dispatch_fused_kernel": ["ep_expert_choice.hip"],
+    "ec_combine_kernel": ["ep_combine.hip"],
+    "rank_pack_kernel": ["ep_rank.hip", "ep_layout.hip"],
+    "rank_sum_kernel": ["ep_rank.hip"],
+}
+
+
+def kernel_source_hash(kernel=None):
+    """SHA-256 over the sources of `kernel` (all of csrc/ when None or not
+    listed), comments and whitespace excluded: a profile summary in
+    profiles/ describes the kernel while this hash is unchanged."""
     d = os.path.join(ROOT, "combine_get_dispatch_04_amd", "csrc")
+    names = sorted(os.listdir(d)) if kernel not in KERNEL_SOURCES else \
+        sorted(["ep_common.h", *KERNEL_SOURCES[kernel]])
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
+    for f in names:
         with open(os.path.join(d, f), encoding="utf-8") as fh:
             h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()
 
 
-def _profile(kind, key):
-    """A committed profile summary (profiles/<kind>_<key>.json), or None when
-    it is missing or was taken on other kernel sources."""
+def _profile_entry(kind, key, kernel):
+    """`kernel`'s entry in a committed profile summary
+    (profiles/<kind>_<key>.json), or None when there is none or it was taken
+    on other sources of that kernel."""
     path = os.path.join(ROOT, "profiles", f"{kind}_{key}.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    return t if t.get("src_sha256") == kernel_source_hash() else None
+    k = t.get("kernels", {}).get(kernel)
+    if k is None or k.get("src_sha256") != kernel_source_hash(kernel):
+        return None
+    return k
 
 
 def traffic_entry(key, kernel):
     """Bytes per launch of `kernel` between L2 and memory (rocprofv3
     FETCH_SIZE + WRITE_SIZE, calibrated), from the committed counter summary
     taken on the current kernel sources; else None."""
-    t = _profile("traffic", key)
-    k = None if t is None else t.get("kernels", {}).get(kernel)
+    k = _profile_entry("traffic", key, kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 def trace_avg_us(key, kernel):
     """Average duration of `kernel` in the committed rocprofv3 kernel trace of
     the same command, taken on the current kernel sources; else None."""
-    t = _profile("kernels", key)
-    k = None if t is None else t.get("kernels", {}).get(kernel)
+    k = _profile_entry("kernels", key, kernel)
     return None if k is None else k.get("avg_us")
 
 

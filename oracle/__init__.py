@@ -108,11 +108,16 @@ def _load(path):
     L.oracle_ec_dispatch.argtypes = [_P, _I, _I, _P, _I, _I, _P, _P]
     L.oracle_ec_invert.argtypes = [_P, _I, _I, _I, _P, _P]
     L.oracle_ec_combine.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P]
+    L.oracle_rank_pack.argtypes = [_P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                                   _P]
+    L.oracle_combine_partial.argtypes = [_P, _I, _P, _P, _I, _I, _P]
+    L.oracle_combine_ranks.argtypes = [_P, _I, _I, _P, _I, _I, _P]
     for f in ("oracle_layout", "oracle_slots", "oracle_dispatch_bf16", "oracle_dispatch_fp8",
               "oracle_combine", "oracle_ec_dispatch", "oracle_ec_invert", "oracle_ec_combine",
               "oracle_e4m3_from_f32_array", "oracle_bf16_from_f64_array",
               "oracle_e5m2_from_f32_array", "oracle_e2m1_from_f32_array",
-              "oracle_dispatch_token_quant", "oracle_dispatch_mx"):
+              "oracle_dispatch_token_quant", "oracle_dispatch_mx", "oracle_rank_pack",
+              "oracle_combine_partial", "oracle_combine_ranks"):
         getattr(L, f).restype = None
     return L
 
@@ -298,4 +303,55 @@ def ec_combine(y: np.ndarray, w: np.ndarray, token_indices: np.ndarray, T: int, 
     n = len(tk) if tk is not None else T
     out = np.empty((n, H), np.uint16)
     lib().oracle_ec_combine(_p(y), _p(w), _p(ti), E, C, H, T, _p(tk), n, _p(out))
+    return out
+
+
+# ---------------------------------------------------------------- one rank's share
+def rank_pack(x: np.ndarray, topk_idx: np.ndarray, w, E: int, R: int, max_rows: int = None):
+    """Sender pack keyed by (destination rank, token) -> dict(rank_offsets
+    [R+1], send_x [rows, H], send_src [rows], send_idx [rows, K], send_w
+    [rows, K] (unit weights where w is None), pack_pos [T, R], num_dropped).
+    Rows past the last kept one keep zeros in send_x, -2 in send_src, -3 in
+    send_idx and nan in send_w."""
+    x = _c(x, np.uint16)
+    idx = _c(topk_idx, np.int32)
+    T, H = x.shape
+    K = idx.shape[1]
+    if max_rows is None:
+        max_rows = T * min(K, R)
+    wa = _c(w, np.float32) if w is not None else None
+    off = np.empty(R + 1, np.int32)
+    sx = np.zeros((max_rows, H), np.uint16)
+    src = np.full(max_rows, -2, np.int32)
+    sidx = np.full((max_rows, K), -3, np.int32)
+    sw = np.full((max_rows, K), np.nan, np.float32)
+    pos = np.empty((T, R), np.int32)
+    nd = np.zeros(1, np.int32)
+    lib().oracle_rank_pack(_p(x), T, H, _p(idx), _p(wa), K, E, R, max_rows, _p(off), _p(sx),
+                           _p(src), _p(sidx), _p(sw), _p(pos), _p(nd))
+    return dict(rank_offsets=off, send_x=sx, send_src=src, send_idx=sidx, send_w=sw,
+                pack_pos=pos, num_dropped=int(nd[0]))
+
+
+def combine_partial(y: np.ndarray, slot: np.ndarray, w=None):
+    """y [rows, H] bf16 bits; slot [S, K]; w [S, K] float32 or None ->
+    partial [S, H] float32."""
+    y = _c(y, np.uint16)
+    slot = _c(slot, np.int32)
+    S, K = slot.shape
+    H = y.shape[1]
+    wa = _c(w, np.float32) if w is not None else None
+    out = np.empty((S, H), np.float32)
+    lib().oracle_combine_partial(_p(y), H, _p(slot), _p(wa), S, K, _p(out))
+    return out
+
+
+def combine_ranks(partial: np.ndarray, pack_pos: np.ndarray):
+    """partial [rows, H] float32; pack_pos [T, R] -> out [T, H] bf16 bits."""
+    pa = _c(partial, np.float32)
+    pos = _c(pack_pos, np.int32)
+    T, R = pos.shape
+    rows, H = pa.shape
+    out = np.empty((T, H), np.uint16)
+    lib().oracle_combine_ranks(_p(pa), rows, H, _p(pos), T, R, _p(out))
     return out

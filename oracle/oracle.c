@@ -30,8 +30,9 @@
  * token-major loops (the dispatch copies and their quantisation, the
  * combines, the expert-choice copy) run their tokens or entries in
  * parallel, each iteration writing its own rows, so the results are the
- * same bytes.  Layout, slots and the inverse map stay serial (a running
- * count), and the OpenMP pragmas are ignored by the plain build.  fp32 is used exactly where the method
+ * same bytes.  Layout, slots, the inverse map and the rank pack stay serial
+ * (a running count), and the OpenMP pragmas are ignored by the plain
+ * build.  fp32 is used exactly where the method
  * fixes it (the fp8 scale and the value that is rounded to e4m3); sums are
  * accumulated in fp64 and rounded once.
  *
@@ -652,6 +653,130 @@ void oracle_ec_combine(const uint16_t *y, const float *w, const int32_t *token_i
         }
         for (int h = 0; h < H; ++h)
             out[(int64_t)o * H + h] = oracle_bf16_from_f64(acc[h]);
+    }
+    free(acc);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* One rank's share of the expert-parallel exchange ([EPA] API         */
+/* Overview: get_dispatch_layout returns num_tokens_per_rank and       */
+/* is_token_in_rank, dispatch sends the tokens to the ranks of their   */
+/* experts and combine reduces what comes back).  Rank r owns experts  */
+/* [r*E/R, (r+1)*E/R).  The exchange itself is not here: what a sender */
+/* packs for rank r is what rank r receives from it.                   */
+/* ------------------------------------------------------------------ */
+
+/* Sender pack: the rows to send, grouped by destination rank.
+ * Readings: a token goes once to each rank that holds at least one of its
+ * valid entries (the is_token_in_rank of the layout), with its whole row
+ * and its entries rewritten for that rank: the local expert id e - r*E/R
+ * where the entry's expert is on r, -1 elsewhere (padding and invalid
+ * entries included), and the entry's weight (1 when w is NULL; 0 where the
+ * id is -1).  Rows are ordered by destination rank, then by token.  With
+ * n_r = tokens sent to rank r, rank_offsets[r] = n_0 + ... + n_{r-1}
+ * (rank_offsets[R] = all rows); the row of (t, r) is rank_offsets[r] +
+ * (number of earlier tokens sent to r), kept only if below max_rows (else
+ * counted in num_dropped, as a contiguous receive buffer drops rows).
+ *   send_x [rows, H], send_src [rows] = t, send_idx / send_w [rows, K]
+ *   (send_w may be NULL), pack_pos [T, R] = the row of (t, r) or -1. */
+void oracle_rank_pack(const uint16_t *x, int T, int H, const int32_t *topk_idx, const float *w,
+                      int K, int E, int R, int max_rows, int32_t *rank_offsets, uint16_t *send_x,
+                      int32_t *send_src, int32_t *send_idx, float *send_w, int32_t *pack_pos,
+                      int32_t *num_dropped)
+{
+    int per_rank = E / R;
+    int64_t row = 0;
+    *num_dropped = 0;
+    for (int64_t i = 0; i < (int64_t)T * R; ++i)
+        pack_pos[i] = -1;
+    for (int r = 0; r < R; ++r) {
+        rank_offsets[r] = (int32_t)row;
+        for (int t = 0; t < T; ++t) {
+            int on_rank = 0;
+            for (int k = 0; k < K; ++k) {
+                int32_t e = topk_idx[(int64_t)t * K + k];
+                if (e >= 0 && e < E && e / per_rank == r)
+                    on_rank = 1;
+            }
+            if (!on_rank)
+                continue;
+            int64_t p = row++;
+            if (p >= max_rows) {
+                (*num_dropped)++;
+                continue;
+            }
+            pack_pos[(int64_t)t * R + r] = (int32_t)p;
+            memcpy(send_x + p * H, x + (int64_t)t * H, (size_t)H * sizeof(uint16_t));
+            send_src[p] = t;
+            for (int k = 0; k < K; ++k) {
+                int32_t e = topk_idx[(int64_t)t * K + k];
+                int here = e >= 0 && e < E && e / per_rank == r;
+                send_idx[p * K + k] = here ? e - r * per_rank : -1;
+                if (send_w)
+                    send_w[p * K + k] = here ? (w ? w[(int64_t)t * K + k] : 1.0f) : 0.0f;
+            }
+        }
+    }
+    rank_offsets[R] = (int32_t)row;
+}
+
+/* The receiving rank's combine before the reverse exchange: per received
+ * row p, partial[p, h] = sum over k with slot >= 0 of w[p,k] * y[slot[p,k], h]
+ * (w NULL = unit weights), taken as the exact sum up to fp64 rounding and
+ * rounded once to fp32.  Reading: the partial sums cross the exchange in
+ * fp32, the accumulator precision of the combine, so the sender's sum of
+ * them is an fp32-accumulated combine as well.  A row with no kept slot
+ * gives +0. */
+void oracle_combine_partial(const uint16_t *y, int H, const int32_t *slot, const float *w, int S,
+                            int K, float *partial)
+{
+#pragma omp parallel
+    {
+    double *acc = (double *)malloc(((size_t)H + 1) * sizeof(double));
+#pragma omp for schedule(static)
+    for (int p = 0; p < S; ++p) {
+        for (int h = 0; h < H; ++h)
+            acc[h] = 0.0;
+        for (int k = 0; k < K; ++k) {
+            int32_t s = slot[(int64_t)p * K + k];
+            if (s < 0)
+                continue;
+            double wk = w ? (double)w[(int64_t)p * K + k] : 1.0;
+            const uint16_t *yr = y + (int64_t)s * H;
+            for (int h = 0; h < H; ++h)
+                acc[h] += wk * (double)oracle_bf16_to_f32(yr[h]);
+        }
+        for (int h = 0; h < H; ++h)
+            partial[(int64_t)p * H + h] = (float)acc[h];
+    }
+    free(acc);
+    }
+}
+
+/* The sender's final sum after the reverse exchange: for token t,
+ * out[t, h] = bf16( sum over r ascending with pack_pos[t,r] in [0, rows) of
+ * partial[pack_pos[t,r], h] ), exact up to fp64 rounding, rounded once; a
+ * token that no rank received gives +0. */
+void oracle_combine_ranks(const float *partial, int rows, int H, const int32_t *pack_pos, int T,
+                          int R, uint16_t *out)
+{
+#pragma omp parallel
+    {
+    double *acc = (double *)malloc(((size_t)H + 1) * sizeof(double));
+#pragma omp for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h)
+            acc[h] = 0.0;
+        for (int r = 0; r < R; ++r) {
+            int32_t p = pack_pos[(int64_t)t * R + r];
+            if (p < 0 || p >= rows)
+                continue;
+            for (int h = 0; h < H; ++h)
+                acc[h] += (double)partial[(int64_t)p * H + h];
+        }
+        for (int h = 0; h < H; ++h)
+            out[(int64_t)t * H + h] = oracle_bf16_from_f64(acc[h]);
     }
     free(acc);
     }

@@ -247,3 +247,53 @@ def mx_quant_row(xrow_bits, fmt):
     if fmt == "mxfp4_e2m1":
         codes = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
     return codes, ecode
+
+
+# ------------------------------------------------------------- one rank's share
+def rank_pack(topk_idx, w, E, R, max_rows):
+    """Sort the distinct (rank, token) pairs of valid entries; the position
+    of a pair in that order is its send row.  Each row carries the token's
+    entries with the experts of that rank as local ids, -1 elsewhere."""
+    T, K = topk_idx.shape
+    per = E // R
+    pairs = sorted({(int(topk_idx[t, k]) // per, t) for t in range(T) for k in range(K)
+                    if 0 <= topk_idx[t, k] < E})
+    off = np.array([sum(1 for r_, _ in pairs if r_ < r) for r in range(R + 1)], np.int32)
+    pos = np.full((T, R), -1, np.int32)
+    rows = []
+    for p, (r, t) in enumerate(pairs):
+        if p >= max_rows:
+            continue
+        pos[t, r] = p
+        ids = [int(topk_idx[t, k]) - r * per
+               if 0 <= topk_idx[t, k] < E and topk_idx[t, k] // per == r else -1
+               for k in range(K)]
+        ws = [(1.0 if w is None else float(w[t, k])) if ids[k] >= 0 else 0.0 for k in range(K)]
+        rows.append((t, ids, ws))
+    return dict(rank_offsets=off, pack_pos=pos, rows=rows,
+                num_dropped=max(0, len(pairs) - max_rows))
+
+
+def combine_partial_f64(y_bits, slot, w):
+    """Per-element loops, fp64 sums, rounded once to fp32."""
+    S, K = slot.shape
+    yf = bf16_to_f64(y_bits)
+    acc = np.zeros((S, y_bits.shape[1]), np.float64)
+    for p in range(S):
+        for k in range(K):
+            if slot[p, k] >= 0:
+                acc[p] += (1.0 if w is None else float(w[p, k])) * yf[slot[p, k]]
+    return acc.astype(np.float32)
+
+
+def combine_ranks_f64(partial, pack_pos):
+    """Per token, the partial rows of its ranks summed in rank order (fp64),
+    rounded once to bf16."""
+    T, R = pack_pos.shape
+    acc = np.zeros((T, partial.shape[1]), np.float64)
+    for t in range(T):
+        for r in range(R):
+            p = pack_pos[t, r]
+            if 0 <= p < partial.shape[0]:
+                acc[t] += partial[p].astype(np.float64)
+    return bf16_nearest_f64(acc.ravel()).reshape(acc.shape)

@@ -28,6 +28,7 @@ TC = "test_oracle_token_choice.py"
 FMT = "test_oracle_formats.py"
 QNT = "test_oracle_quant.py"
 EC = "test_oracle_expert_choice.py"
+RK = "test_oracle_ranks.py"
 
 # (what, exact text in oracle.c, replacement, pin module that must catch it)
 MUTANTS = [
@@ -107,6 +108,27 @@ MUTANTS = [
     ("expert choice: combine weights ignored",
      "acc[h] += (double)w[j] * (double)oracle_bf16_to_f32(yr[h]);",
      "acc[h] += (double)oracle_bf16_to_f32(yr[h]);", EC),
+    ("rank pack: rank of an expert taken modulo R",
+     "if (e >= 0 && e < E && e / per_rank == r)\n                    on_rank = 1;",
+     "if (e >= 0 && e < E && e % R == r)\n                    on_rank = 1;", RK),
+    ("rank pack: local id not shifted",
+     "send_idx[p * K + k] = here ? e - r * per_rank : -1;", "send_idx[p * K + k] = here ? e : -1;",
+     RK),
+    ("rank pack: other ranks' weights kept",
+     "send_w[p * K + k] = here ? (w ? w[(int64_t)t * K + k] : 1.0f) : 0.0f;",
+     "send_w[p * K + k] = w ? w[(int64_t)t * K + k] : 1.0f;", RK),
+    ("rank pack: dropped rows not counted",
+     "            if (p >= max_rows) {\n                (*num_dropped)++;",
+     "            if (p >= max_rows) {\n", RK),
+    ("partial combine: rounded to bf16 instead of fp32",
+     "partial[(int64_t)p * H + h] = (float)acc[h];",
+     "partial[(int64_t)p * H + h] = oracle_bf16_to_f32(oracle_bf16_from_f64(acc[h]));", RK),
+    ("partial combine: weights ignored",
+     "double wk = w ? (double)w[(int64_t)p * K + k] : 1.0;", "double wk = 1.0;", RK),
+    ("rank sum: the last rank left out",
+     "        for (int r = 0; r < R; ++r) {\n            int32_t p = pack_pos[(int64_t)t * R + r];",
+     "        for (int r = 0; r + 1 < R; ++r) {\n            int32_t p = pack_pos[(int64_t)t * R + r];",
+     RK),
 ]
 
 
