@@ -31,6 +31,8 @@ SIGNATURES = {
     "ep_low_latency_dispatch": (_ST, [_P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                                       _P, _P]),
     "ep_combine": (_ST, [_P, _I, _I, _P, _P, _I, _I, _P, _P]),
+    "ep_layout_dispatch_noalloc": (_ST, [_P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I,
+                                         _I, _P, _P, _P, _P, _P, _P]),
     "ep_dispatch_expert_choice": (_ST, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "ep_combine_expert_choice": (_ST, [_P, _P, _I, _I, _I, _P, _P, _I, _P, _P]),
 }
@@ -99,6 +101,17 @@ def ep_low_latency_dispatch(x, T, H, topk_idx, K, E, cap, quant, recv_x, recv_sc
                                        slot, recv_src, recv_count, num_dropped, num_invalid,
                                        stream)
     return _check("ep_low_latency_dispatch", st) if check else st
+
+
+def ep_layout_dispatch_noalloc(x, T, H, topk_idx, K, E, R, counts, offsets, tokens_per_rank,
+                               is_token_in_rank, num_invalid, layout, cap_or_max_rows, quant,
+                               recv_x, recv_scales, slot, recv_src, num_dropped, stream,
+                               check=True):
+    st = lib().ep_layout_dispatch_noalloc(x, T, H, topk_idx, K, E, R, counts, offsets,
+                                          tokens_per_rank, is_token_in_rank, num_invalid, layout,
+                                          cap_or_max_rows, quant, recv_x, recv_scales, slot,
+                                          recv_src, num_dropped, stream)
+    return _check("ep_layout_dispatch_noalloc", st) if check else st
 
 
 def ep_combine(y, y_rows, H, slot, topk_weights, T, K, out, stream, check=True):

@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "ep_internal.h"
 
 namespace {
@@ -38,6 +40,93 @@ ep_status_t check_ws(const void *ws, size_t ws_bytes, size_t need)
     if (!ws || !aligned(ws, 256) || ws_bytes < need)
         return EP_ERR_WORKSPACE;
     return EP_OK;
+}
+
+// The arguments of a dispatch (ep_dispatch and the no-allocation form),
+// other than the workspace.
+ep_status_t check_dispatch_args(const uint16_t *x, int T, int H, const int32_t *topk_idx, int K,
+                                int E, const int32_t *offsets, ep_recv_layout_t layout,
+                                int cap_or_max_rows, ep_quant_t quant, const void *recv_x,
+                                const void *recv_scales, const int32_t *slot,
+                                const int32_t *recv_src, const int32_t *num_dropped)
+{
+    ep_status_t st = check_layout_sizes(T, K, E, 1);
+    if (st != EP_OK)
+        return st;
+    if (layout != EP_LAYOUT_CONTIGUOUS && layout != EP_LAYOUT_PADDED)
+        return EP_ERR_INVALID_ARG;
+    if ((int)quant < (int)EP_QUANT_BF16 || (int)quant > (int)EP_QUANT_MXFP4_E2M1)
+        return EP_ERR_INVALID_ARG;
+    const bool quantised = quant != EP_QUANT_BF16;
+    const bool mx = quant == EP_QUANT_MXFP8_E4M3 || quant == EP_QUANT_MXFP8_E5M2 ||
+                    quant == EP_QUANT_MXFP4_E2M1;
+    const bool padded = layout == EP_LAYOUT_PADDED;
+    if (H < 8 || H % 8 != 0 || (quant == EP_QUANT_FP8_E4M3_G128 && H % 128 != 0) ||
+        (mx && H % 32 != 0))
+        return EP_ERR_INVALID_ARG;
+    if (H > kMaxHidden)
+        return EP_ERR_UNSUPPORTED;
+    if (cap_or_max_rows < 0)
+        return EP_ERR_INVALID_ARG;
+    const int64_t rows = padded ? (int64_t)E * cap_or_max_rows : cap_or_max_rows;
+    if (rows > kI32)
+        return EP_ERR_INVALID_ARG;
+    if (!offsets || !num_dropped || (T > 0 && (!x || !topk_idx || !slot)) ||
+        (rows > 0 && T > 0 && !recv_x) || (quantised && rows > 0 && T > 0 && !recv_scales))
+        return EP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || (!mx && !aligned(recv_scales, 4)) ||
+        !aligned(topk_idx, 4) || !aligned(offsets, 4) || !aligned(slot, 4) ||
+        !aligned(recv_src, 4) || !aligned(num_dropped, 4))
+        return EP_ERR_INVALID_ARG;
+    return EP_OK;
+}
+
+// Scratch of ep_layout_dispatch_noalloc: the layout's per-chunk tables and
+// per-entry ranks, which the dispatch then reads (what the workspace holds
+// for the pair).  Each device holds its own copy for the life of the
+// process.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): it uses the device address
+// that hipGetSymbolAddress returned for the device, taken once per device
+// with that device current.
+__device__ __align__(256) char scratch[EP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the device that runs `stream`, or
+// nullptr if the runtime cannot give it.
+char *scratch_for(hipStream_t stream)
+{
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int cur = -1, dev = -1;
+    if (hipGetDevice(&cur) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    dev = cur;
+    if (stream && (hipStreamGetDevice(stream, &dev) != hipSuccess)) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur)
+            (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return static_cast<char *>(addr[dev]);
 }
 
 }  // namespace
@@ -102,42 +191,61 @@ ep_status_t ep_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx
                         int32_t *recv_src, int32_t *num_dropped, void *ws, size_t ws_bytes,
                         void *stream)
 {
-    ep_status_t st = check_layout_sizes(T, K, E, 1);
+    ep_status_t st = check_dispatch_args(x, T, H, topk_idx, K, E, offsets, layout,
+                                         cap_or_max_rows, quant, recv_x, recv_scales, slot,
+                                         recv_src, num_dropped);
     if (st != EP_OK)
         return st;
-    if (layout != EP_LAYOUT_CONTIGUOUS && layout != EP_LAYOUT_PADDED)
-        return EP_ERR_INVALID_ARG;
-    if ((int)quant < (int)EP_QUANT_BF16 || (int)quant > (int)EP_QUANT_MXFP4_E2M1)
-        return EP_ERR_INVALID_ARG;
-    const bool quantised = quant != EP_QUANT_BF16;
-    const bool mx = quant == EP_QUANT_MXFP8_E4M3 || quant == EP_QUANT_MXFP8_E5M2 ||
-                    quant == EP_QUANT_MXFP4_E2M1;
-    const bool padded = layout == EP_LAYOUT_PADDED;
-    if (H < 8 || H % 8 != 0 || (quant == EP_QUANT_FP8_E4M3_G128 && H % 128 != 0) ||
-        (mx && H % 32 != 0))
-        return EP_ERR_INVALID_ARG;
-    if (H > kMaxHidden)
-        return EP_ERR_UNSUPPORTED;
-    if (cap_or_max_rows < 0)
-        return EP_ERR_INVALID_ARG;
-    const int64_t rows = padded ? (int64_t)E * cap_or_max_rows : cap_or_max_rows;
-    if (rows > kI32)
-        return EP_ERR_INVALID_ARG;
-    if (!offsets || !num_dropped || (T > 0 && (!x || !topk_idx || !slot)) ||
-        (rows > 0 && T > 0 && !recv_x) || (quantised && rows > 0 && T > 0 && !recv_scales))
-        return EP_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || !aligned(recv_x, 16) || (!mx && !aligned(recv_scales, 4)) ||
-        !aligned(topk_idx, 4) || !aligned(offsets, 4) || !aligned(slot, 4) ||
-        !aligned(recv_src, 4) || !aligned(num_dropped, 4))
-        return EP_ERR_INVALID_ARG;
     ep::LayoutPlan p = ep::make_layout_plan(T, K, E, 1);
     if ((st = check_ws(ws, ws_bytes, p.bytes)) != EP_OK)
         return st;
-    return hip_status(ep::launch_dispatch(p, x, H, topk_idx, offsets, padded, cap_or_max_rows,
+    return hip_status(ep::launch_dispatch(p, x, H, topk_idx, offsets,
+                                          layout == EP_LAYOUT_PADDED, cap_or_max_rows,
                                           (int)quant,
                                           recv_x, recv_scales, slot, recv_src, num_dropped,
                                           static_cast<char *>(ws),
                                           static_cast<hipStream_t>(stream)));
+}
+
+ep_status_t ep_layout_dispatch_noalloc(const uint16_t *x, int T, int H, const int32_t *topk_idx,
+                                       int K, int E, int R, int32_t *counts, int32_t *offsets,
+                                       int32_t *tokens_per_rank, uint8_t *is_token_in_rank,
+                                       int32_t *num_invalid, ep_recv_layout_t layout,
+                                       int cap_or_max_rows, ep_quant_t quant, void *recv_x,
+                                       void *recv_scales, int32_t *slot, int32_t *recv_src,
+                                       int32_t *num_dropped, void *stream)
+{
+    // every check of ep_get_dispatch_layout and ep_dispatch, then the size
+    // check, all before anything is enqueued
+    ep_status_t st = check_layout_sizes(T, K, E, R);
+    if (st != EP_OK)
+        return st;
+    if ((T > 0 && !topk_idx) || !counts || !offsets || !num_invalid)
+        return EP_ERR_INVALID_ARG;
+    if (!aligned(counts, 4) || !aligned(tokens_per_rank, 4) || !aligned(num_invalid, 4))
+        return EP_ERR_INVALID_ARG;
+    st = check_dispatch_args(x, T, H, topk_idx, K, E, offsets, layout, cap_or_max_rows, quant,
+                             recv_x, recv_scales, slot, recv_src, num_dropped);
+    if (st != EP_OK)
+        return st;
+    const ep::LayoutPlan pl = ep::make_layout_plan(T, K, E, R);
+    const ep::LayoutPlan pd = ep::make_layout_plan(T, K, E, 1);
+    if (pl.bytes > EP_NOALLOC_SCRATCH_BYTES || pd.bytes > EP_NOALLOC_SCRATCH_BYTES)
+        return EP_ERR_UNSUPPORTED;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = scratch_for(s);
+    if (!ws)
+        return EP_ERR_HIP;
+    // the layout writes every table entry the dispatch reads, so the
+    // scratch needs no clearing between calls
+    hipError_t e = ep::launch_layout(pl, topk_idx, counts, offsets, tokens_per_rank,
+                                     is_token_in_rank, num_invalid, ws, s);
+    if (e != hipSuccess)
+        return EP_ERR_HIP;
+    return hip_status(ep::launch_dispatch(pd, x, H, topk_idx, offsets,
+                                          layout == EP_LAYOUT_PADDED, cap_or_max_rows,
+                                          (int)quant, recv_x, recv_scales, slot, recv_src,
+                                          num_dropped, ws, s));
 }
 
 ep_status_t ep_low_latency_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx,

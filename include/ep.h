@@ -209,6 +209,40 @@ ep_status_t ep_low_latency_dispatch(const uint16_t *x, int T, int H, const int32
                                     int32_t *num_invalid, void *stream);
 
 /*
+ * ep_layout_dispatch_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): ep_get_dispatch_layout followed by ep_dispatch in one
+ * call, with no workspace argument.  The per-chunk tables and per-entry
+ * ranks that the pair keeps in `ws` live instead in a device array inside
+ * the library, EP_NOALLOC_SCRATCH_BYTES per device, held from the library's
+ * first call on that device until the process ends.  Every output (counts,
+ * offsets, tokens_per_rank, is_token_in_rank, num_invalid, recv_x,
+ * recv_scales, slot, recv_src, num_dropped) is exactly the pair's for the
+ * same arguments, which follow the two calls' rules (R as in
+ * ep_get_dispatch_layout).
+ *   - Nothing is allocated: no hipMalloc, no workspace, no allocating
+ *     library routine.  The caller still provides every input and output.
+ *   - Sizes whose tables exceed the array (ep_workspace_bytes(T, K, E, R) >
+ *     EP_NOALLOC_SCRATCH_BYTES, e.g. T*K beyond about 1.9 million entries)
+ *     return EP_ERR_UNSUPPORTED with nothing enqueued: use the pair.
+ *   - All calls on one device share its array, and each call's layout
+ *     rewrites every entry the dispatch then reads, so nothing needs
+ *     clearing; but two calls whose work overlaps on one device (on
+ *     different streams, or from different threads) race on the array and
+ *     give undefined results.  Serialise them.
+ *   - EP_ERR_HIP also when the runtime cannot give the array's address on
+ *     the stream's device.
+ */
+#define EP_NOALLOC_SCRATCH_BYTES (8u << 20)
+ep_status_t ep_layout_dispatch_noalloc(const uint16_t *x, int T, int H, const int32_t *topk_idx,
+                                       int K, int E, int R, int32_t *counts, int32_t *offsets,
+                                       int32_t *tokens_per_rank, uint8_t *is_token_in_rank,
+                                       int32_t *num_invalid, ep_recv_layout_t layout,
+                                       int cap_or_max_rows, ep_quant_t quant, void *recv_x,
+                                       void *recv_scales, int32_t *slot, int32_t *recv_src,
+                                       int32_t *num_dropped, void *stream);
+
+/*
  * ep_combine -- [EPA] API Overview, combine (reduce through the dispatch
  * handle) and low_latency_combine (also takes topk_weights).
  *   out[t, :] = bf16( sum over k with slot[t,k] >= 0 of w[t,k] * y[slot[t,k], :] )

@@ -139,6 +139,48 @@ def test_dispatch_rejects(kw, status):
     assert _dispatch(**kw) == status
 
 
+def _noalloc(**kw):
+    args = dict(x=A, T=16, H=256, topk_idx=A, K=2, E=8, R=1, counts=A, offsets=A,
+                tokens_per_rank=A, is_token_in_rank=A, num_invalid=A, layout=0,
+                cap_or_max_rows=32, quant=0, recv_x=B, recv_scales=None, slot=A, recv_src=A,
+                num_dropped=A, stream=None)
+    args.update(kw)
+    return N.ep_layout_dispatch_noalloc(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=0), N.EP_ERR_INVALID_ARG),
+    (dict(E=8, R=3), N.EP_ERR_INVALID_ARG),
+    (dict(R=2048, E=2048), N.EP_ERR_UNSUPPORTED),
+    (dict(counts=None), N.EP_ERR_INVALID_ARG),
+    (dict(num_invalid=A + 2), N.EP_ERR_INVALID_ARG),
+    (dict(H=12), N.EP_ERR_INVALID_ARG),
+    (dict(quant=1, recv_scales=None), N.EP_ERR_INVALID_ARG),
+    (dict(layout=5), N.EP_ERR_INVALID_ARG),
+    (dict(x=A + 8), N.EP_ERR_INVALID_ARG),
+    (dict(slot=None), N.EP_ERR_INVALID_ARG),
+    # tables beyond the library's scratch array (8 MiB): use the pair instead
+    (dict(T=1 << 20, K=4, cap_or_max_rows=1 << 22), N.EP_ERR_UNSUPPORTED),
+    (dict(T=600000, K=4, cap_or_max_rows=2400000), N.EP_ERR_UNSUPPORTED),
+])
+def test_noalloc_rejects(kw, status):
+    """Rejected on the host before anything is enqueued, like the pair;
+    sizes whose tables exceed the scratch array are refused."""
+    assert _noalloc(**kw) == status
+
+
+def test_noalloc_limit_is_the_pair_workspace():
+    """The size limit is ep_workspace_bytes of the pair against the
+    scratch array's EP_NOALLOC_SCRATCH_BYTES (8 MiB): the prefill and large
+    workloads fit, with room for several times their token counts."""
+    lim = 8 << 20
+    assert re.search(r"#define\s+EP_NOALLOC_SCRATCH_BYTES\s+\(8u << 20\)", open(HEADER).read())
+    assert N.ep_workspace_bytes(4096, 8, 256, 8) <= lim
+    assert N.ep_workspace_bytes(16384, 16, 384, 32) <= lim
+    assert N.ep_workspace_bytes(65536, 16, 384, 32) <= lim
+    assert N.ep_workspace_bytes(600000, 4, 8, 1) > lim
+
+
 def _ll(**kw):
     args = dict(x=A, T=16, H=256, topk_idx=A, K=2, E=8, cap=4, quant=0, recv_x=B,
                 recv_scales=None, slot=A, recv_src=A, recv_count=A, num_dropped=A,
