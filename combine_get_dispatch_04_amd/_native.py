@@ -33,6 +33,11 @@ SIGNATURES = {
     "ep_combine": (_ST, [_P, _I, _I, _P, _P, _I, _I, _P, _P]),
     "ep_layout_dispatch_noalloc": (_ST, [_P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I,
                                          _I, _P, _P, _P, _P, _P, _P]),
+    "ep_pack_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "ep_pack_by_rank": (_ST, [_P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                              _P, _SZ, _P]),
+    "ep_combine_partial": (_ST, [_P, _I, _I, _P, _P, _I, _I, _P, _P]),
+    "ep_combine_ranks": (_ST, [_P, _I, _I, _P, _I, _I, _P, _P]),
     "ep_dispatch_expert_choice": (_ST, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "ep_combine_expert_choice": (_ST, [_P, _P, _I, _I, _I, _P, _P, _I, _P, _P]),
 }
@@ -129,3 +134,26 @@ def ep_dispatch_expert_choice(x, T, H, token_indices, E, C, recv_x, tok_off, tok
 def ep_combine_expert_choice(y, weights, E, C, H, tok_off, tok_ent, T, out, stream, check=True):
     st = lib().ep_combine_expert_choice(y, weights, E, C, H, tok_off, tok_ent, T, out, stream)
     return _check("ep_combine_expert_choice", st) if check else st
+
+
+def ep_pack_workspace_bytes(T: int, K: int, E: int, R: int) -> int:
+    return lib().ep_pack_workspace_bytes(T, K, E, R)
+
+
+def ep_pack_by_rank(x, T, H, topk_idx, topk_weights, K, E, R, max_rows, tokens_per_rank,
+                    rank_offsets, send_x, send_src, send_idx, send_w, pack_pos, num_dropped, ws,
+                    ws_bytes, stream, check=True):
+    st = lib().ep_pack_by_rank(x, T, H, topk_idx, topk_weights, K, E, R, max_rows,
+                               tokens_per_rank, rank_offsets, send_x, send_src, send_idx, send_w,
+                               pack_pos, num_dropped, ws, ws_bytes, stream)
+    return _check("ep_pack_by_rank", st) if check else st
+
+
+def ep_combine_partial(y, y_rows, H, slot, weights, S, K, partial, stream, check=True):
+    st = lib().ep_combine_partial(y, y_rows, H, slot, weights, S, K, partial, stream)
+    return _check("ep_combine_partial", st) if check else st
+
+
+def ep_combine_ranks(partial, rows, H, pack_pos, T, R, out, stream, check=True):
+    st = lib().ep_combine_ranks(partial, rows, H, pack_pos, T, R, out, stream)
+    return _check("ep_combine_ranks", st) if check else st

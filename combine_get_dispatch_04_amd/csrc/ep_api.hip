@@ -300,6 +300,78 @@ ep_status_t ep_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t ep_pack_workspace_bytes(int T, int K, int E, int R)
+{
+    if (check_layout_sizes(T, K, E, R) != EP_OK)
+        return 0;
+    return ep::make_rank_plan(T, K, E, R).bytes;
+}
+
+ep_status_t ep_pack_by_rank(const uint16_t *x, int T, int H, const int32_t *topk_idx,
+                            const float *topk_weights, int K, int E, int R, int max_rows,
+                            int32_t *tokens_per_rank, int32_t *rank_offsets, uint16_t *send_x,
+                            int32_t *send_src, int32_t *send_idx, float *send_w,
+                            int32_t *pack_pos, int32_t *num_dropped, void *ws, size_t ws_bytes,
+                            void *stream)
+{
+    ep_status_t st = check_layout_sizes(T, K, E, R);
+    if (st != EP_OK)
+        return st;
+    if (H < 8 || H % 8 != 0 || max_rows < 0)
+        return EP_ERR_INVALID_ARG;
+    if (H > kMaxHidden)
+        return EP_ERR_UNSUPPORTED;
+    if (!tokens_per_rank || !rank_offsets || !num_dropped ||
+        (T > 0 && (!x || !topk_idx || !pack_pos)) ||
+        (T > 0 && max_rows > 0 && (!send_x || !send_src || !send_idx)))
+        return EP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(send_x, 16) || !aligned(topk_idx, 4) ||
+        !aligned(topk_weights, 4) || !aligned(tokens_per_rank, 4) || !aligned(rank_offsets, 4) ||
+        !aligned(send_src, 4) || !aligned(send_idx, 4) || !aligned(send_w, 4) ||
+        !aligned(pack_pos, 4) || !aligned(num_dropped, 4))
+        return EP_ERR_INVALID_ARG;
+    if ((int64_t)T * R > kI32 || (int64_t)max_rows * K > kI32)
+        return EP_ERR_INVALID_ARG;
+    const ep::RankPlan rp = ep::make_rank_plan(T, K, E, R);
+    if ((st = check_ws(ws, ws_bytes, rp.bytes)) != EP_OK)
+        return st;
+    return hip_status(ep::launch_rank_pack(rp, x, H, topk_idx, topk_weights, E, R, max_rows,
+                                           tokens_per_rank, rank_offsets, send_x, send_src,
+                                           send_idx, send_w, pack_pos, num_dropped,
+                                           static_cast<char *>(ws),
+                                           static_cast<hipStream_t>(stream)));
+}
+
+ep_status_t ep_combine_partial(const uint16_t *y, int y_rows, int H, const int32_t *slot,
+                               const float *weights, int S, int K, float *partial, void *stream)
+{
+    if (S < 0 || K < 1 || H < 8 || H % 8 != 0 || (int64_t)S * K > kI32 || y_rows < 0)
+        return EP_ERR_INVALID_ARG;
+    if (H > kMaxHidden)
+        return EP_ERR_UNSUPPORTED;
+    if (S > 0 && (!slot || !partial || (y_rows > 0 && !y)))
+        return EP_ERR_INVALID_ARG;
+    if (!aligned(y, 16) || !aligned(partial, 16) || !aligned(slot, 4) || !aligned(weights, 4))
+        return EP_ERR_INVALID_ARG;
+    return hip_status(ep::launch_combine_partial(y, y_rows, H, slot, weights, S, K, partial,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+ep_status_t ep_combine_ranks(const float *partial, int rows, int H, const int32_t *pack_pos,
+                             int T, int R, uint16_t *out, void *stream)
+{
+    if (T < 0 || R < 1 || rows < 0 || H < 8 || H % 8 != 0 || (int64_t)T * R > kI32)
+        return EP_ERR_INVALID_ARG;
+    if (R > kMaxRanks || H > kMaxHidden)
+        return EP_ERR_UNSUPPORTED;
+    if (T > 0 && (!pack_pos || !out || (rows > 0 && !partial)))
+        return EP_ERR_INVALID_ARG;
+    if (!aligned(partial, 16) || !aligned(out, 16) || !aligned(pack_pos, 4))
+        return EP_ERR_INVALID_ARG;
+    return hip_status(ep::launch_rank_sum(partial, rows, H, pack_pos, T, R, out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 ep_status_t ep_dispatch_expert_choice(const uint16_t *x, int T, int H,
                                       const int32_t *token_indices, int E, int C,
                                       uint16_t *recv_x, int32_t *tok_off, int32_t *tok_ent,

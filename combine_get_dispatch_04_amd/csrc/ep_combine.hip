@@ -15,6 +15,10 @@
 // y row is read once) and accumulates with fp32 FMAs in ascending k / entry
 // order, then rounds once to bf16 (nearest even).  A token with no source
 // row writes +0.
+//
+// The receiving rank of the expert-parallel exchange uses the token-choice
+// kernel with fp32 output rows (F32): its partial sums per received row
+// travel back to the sender, which adds them over ranks (ep_rank.hip).
 #include "ep_common.h"
 #include "ep_internal.h"
 
@@ -44,33 +48,43 @@ __device__ __forceinline__ void acc_row(float (&acc)[PPT][8], const char *src, f
     }
 }
 
-template <int PPT>
-__device__ __forceinline__ void store_row(const float (&acc)[PPT][8], uint16_t *out, int H, int t,
+// bf16 rows (16 bytes per 8 channels), or fp32 rows (32 bytes) when F32.
+template <int PPT, bool F32 = false>
+__device__ __forceinline__ void store_row(const float (&acc)[PPT][8], void *out, int H, int t,
                                           int seg0, int pieces)
 {
-    char *dst = reinterpret_cast<char *>(out) + (size_t)t * H * 2;
+    char *dst = reinterpret_cast<char *>(out) + (size_t)t * H * (F32 ? 4 : 2);
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
         int i = seg0 + threadIdx.x + j * blockDim.x;
         if (i < pieces) {
-            u32x4 o;
-            o.x = pack_bf16x2(acc[j][0], acc[j][1]);
-            o.y = pack_bf16x2(acc[j][2], acc[j][3]);
-            o.z = pack_bf16x2(acc[j][4], acc[j][5]);
-            o.w = pack_bf16x2(acc[j][6], acc[j][7]);
-            st16(dst + (size_t)i * 16, o);
+            if constexpr (F32) {
+                st16(dst + (size_t)i * 32, u32x4{__float_as_uint(acc[j][0]), __float_as_uint(acc[j][1]),
+                                                 __float_as_uint(acc[j][2]), __float_as_uint(acc[j][3])});
+                st16(dst + (size_t)i * 32 + 16,
+                     u32x4{__float_as_uint(acc[j][4]), __float_as_uint(acc[j][5]),
+                           __float_as_uint(acc[j][6]), __float_as_uint(acc[j][7])});
+            } else {
+                u32x4 o;
+                o.x = pack_bf16x2(acc[j][0], acc[j][1]);
+                o.y = pack_bf16x2(acc[j][2], acc[j][3]);
+                o.z = pack_bf16x2(acc[j][4], acc[j][5]);
+                o.w = pack_bf16x2(acc[j][6], acc[j][7]);
+                st16(dst + (size_t)i * 16, o);
+            }
         }
     }
 }
 
 // G == 1: one source row per round, its slot and weight scalar loads; slots
 // outside [0, y_rows) are skipped.  G > 1: G valid source rows per round,
-// all G*PPT row pieces requested before the first FMA.
-template <int PPT, int G>
+// all G*PPT row pieces requested before the first FMA.  F32: fp32 output
+// rows (the partial sums of the exchange) instead of bf16.
+template <int PPT, int G, bool F32 = false>
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint16_t *__restrict__ y, int y_rows, int H,
                const int32_t *__restrict__ slot, const float *__restrict__ w, int K,
-               uint16_t *__restrict__ out)
+               void *__restrict__ out)
 {
     const int t = blockIdx.x;
     const int pieces = H >> 3;
@@ -148,7 +162,7 @@ combine_kernel(const uint16_t *__restrict__ y, int y_rows, int H,
             }
         }
     }
-    store_row<PPT>(acc, out, H, t, seg0, pieces);
+    store_row<PPT, F32>(acc, out, H, t, seg0, pieces);
 }
 
 // G entries per round: their row indices and weights are scalar loads, then
@@ -252,8 +266,9 @@ RowShape row_shape(int pieces, int maxppt)
         return hipErrorInvalidValue; \
     }
 
-hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot,
-                          const float *w, int T, int K, uint16_t *out, hipStream_t s)
+template <bool F32>
+hipError_t launch_combine_t(const uint16_t *y, int y_rows, int H, const int32_t *slot,
+                            const float *w, int T, int K, void *out, hipStream_t s)
 {
     if (T == 0)
         return hipSuccess;
@@ -271,21 +286,33 @@ hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *s
     dim3 grid(T, rs.nseg), block(rs.bd);
 #define EP_COMBINE_CASE(N)                                                                       \
     case N:                                                                                      \
-        hipLaunchKernelGGL((combine_kernel<N, 1>), grid, block, 0, s, y, y_rows, H, slot, w, K, \
-                           out);                                                         \
+        hipLaunchKernelGGL((combine_kernel<N, 1, F32>), grid, block, 0, s, y, y_rows, H, slot, w, \
+                           K, out);                                                              \
         break;
     if (many) {
         if (rs.ppt == 1)
-            hipLaunchKernelGGL((combine_kernel<1, 4>), grid, block, 0, s, y, y_rows, H, slot, w,
-                               K, out);
+            hipLaunchKernelGGL((combine_kernel<1, 4, F32>), grid, block, 0, s, y, y_rows, H, slot,
+                               w, K, out);
         else
-            hipLaunchKernelGGL((combine_kernel<2, 4>), grid, block, 0, s, y, y_rows, H, slot, w,
-                               K, out);
+            hipLaunchKernelGGL((combine_kernel<2, 4, F32>), grid, block, 0, s, y, y_rows, H, slot,
+                               w, K, out);
         return hipGetLastError();
     }
     EP_PPT_SWITCH(rs.ppt, EP_COMBINE_CASE)
 #undef EP_COMBINE_CASE
     return hipGetLastError();
+}
+
+hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot,
+                          const float *w, int T, int K, uint16_t *out, hipStream_t s)
+{
+    return launch_combine_t<false>(y, y_rows, H, slot, w, T, K, out, s);
+}
+
+hipError_t launch_combine_partial(const uint16_t *y, int y_rows, int H, const int32_t *slot,
+                                  const float *w, int S, int K, float *partial, hipStream_t s)
+{
+    return launch_combine_t<true>(y, y_rows, H, slot, w, S, K, partial, s);
 }
 
 hipError_t launch_ec_combine(const uint16_t *y, const float *w, int E, int C, int H,

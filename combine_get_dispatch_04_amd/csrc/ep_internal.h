@@ -16,6 +16,9 @@ struct LayoutPlan {
     int waves;     // waves per chunk block
     int epl;       // entries per lane (1..32, a power of two)
     int nbits;     // bits needed for an expert id in [0, E)
+    // rank keys (the sender pack): E counts ranks, the entries hold experts
+    // in [0, key_experts), key_div per rank; key_div == 0 for expert keys
+    int key_experts, key_div;
     size_t lds;    // dynamic shared memory of the chunk kernel
     // workspace carve-up (byte offsets, 256-aligned)
     // off_tamax: [T] fp32 row maxima for the per-token modes when a row spans
@@ -24,6 +27,14 @@ struct LayoutPlan {
 };
 
 LayoutPlan make_layout_plan(int T, int K, int E, int R);
+
+// The layout of the sender pack: rank keys over R ranks of E/R experts each,
+// plus room for its invalid-entry count (off_misc) in the workspace.
+struct RankPlan {
+    LayoutPlan lp;
+    size_t off_misc, bytes;
+};
+RankPlan make_rank_plan(int T, int K, int E, int R);
 
 struct EcPlan {
     int T, E, C;
@@ -62,6 +73,20 @@ hipError_t launch_ll_dispatch(const uint16_t *x, int T, int H, const int32_t *to
 
 hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot,
                           const float *w, int T, int K, uint16_t *out, hipStream_t s);
+
+// The combine with fp32 output rows: the receiving rank's partial sums.
+hipError_t launch_combine_partial(const uint16_t *y, int y_rows, int H, const int32_t *slot,
+                                  const float *w, int S, int K, float *partial, hipStream_t s);
+
+// The sender pack (rank layout + rank_pack_kernel) and the sender's sum of
+// the partials over ranks (ep_rank.hip).
+hipError_t launch_rank_pack(const RankPlan &rp, const uint16_t *x, int H, const int32_t *topk_idx,
+                            const float *w, int E, int R, int max_rows, int32_t *tokens_per_rank,
+                            int32_t *rank_offsets, uint16_t *send_x, int32_t *send_src,
+                            int32_t *send_idx, float *send_w, int32_t *pack_pos,
+                            int32_t *num_dropped, char *ws, hipStream_t s);
+hipError_t launch_rank_sum(const float *partial, int rows, int H, const int32_t *pack_pos, int T,
+                           int R, uint16_t *out, hipStream_t s);
 
 hipError_t launch_ec_dispatch(const EcPlan &p, const uint16_t *x, int H,
                               const int32_t *token_indices, uint16_t *recv_x, int32_t *tok_off,

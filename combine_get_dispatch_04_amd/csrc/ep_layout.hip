@@ -17,6 +17,12 @@
 // lanes x 8 entries), that block does this itself and there is one launch.
 // ep_dispatch later places entry (t,k) of expert e at
 // offsets[e] + chunk_base[t / CT][e] + local_rank[t, k].
+//
+// The sender pack of the expert-parallel exchange uses the same sort with
+// ranks for keys ("rank keys"): entry (t,k) is keyed by the rank of its
+// expert when it is the first of token t's valid entries on that rank, and
+// is padding otherwise, so each key's entries are the tokens sent to that
+// rank in token order, and the counts are the tokens per rank.
 #include <algorithm>
 #include <atomic>
 
@@ -65,7 +71,8 @@ __device__ void offsets_from_totals(const int32_t *tot, int E, int32_t *offsets,
 // compact (not unrolled) and their state lives in shared memory.
 __global__ void __launch_bounds__(1024)
 layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, int R, int CT,
-                    int nbits, int epl, int32_t *__restrict__ chunk_hist,
+                    int nbits, int epl, int key_experts, int key_div,
+                    int32_t *__restrict__ chunk_hist,
                     int32_t *__restrict__ local_rank, int32_t *__restrict__ rank_part,
                     int32_t *__restrict__ inval_part, uint8_t *__restrict__ is_token_in_rank,
                     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
@@ -113,6 +120,34 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
     if (tid < 32)
         tmp[tid] = 0;
     __syncthreads();
+
+    // ---- rank keys: E here counts ranks; the entries hold experts in
+    // [0, key_experts), key_div of them per rank.  An entry keeps its rank if
+    // no earlier entry of its token has a valid expert on that rank, and
+    // becomes padding (-1) otherwise; an invalid expert stays invalid (-2).
+    if (key_div > 0) {
+        for (int i = tid; i < n; i += blockDim.x) {
+            const int tl = i / K, k = i - tl * K;
+            const int e = ent[i];
+            int key = e == -1 ? -1 : -2;
+            if ((unsigned)e < (unsigned)key_experts) {
+                const int r = e / key_div;
+                key = r;
+                for (int k2 = 0; k2 < k; ++k2) {
+                    const int e2 = ent[tl * K + k2];
+                    if ((unsigned)e2 < (unsigned)key_experts && e2 / key_div == r) {
+                        key = -1;
+                        break;
+                    }
+                }
+            }
+            rkl[i] = key;
+        }
+        __syncthreads();
+        for (int i = tid; i < n; i += blockDim.x)
+            ent[i] = rkl[i];
+        __syncthreads();
+    }
 
     // ---- stable ranks inside the wave's run: running count + same-expert lanes below
     int32_t *myh = whist + w * E;
@@ -396,6 +431,17 @@ LayoutPlan make_layout_plan(int T, int K, int E, int R)
     return p;
 }
 
+RankPlan make_rank_plan(int T, int K, int E, int R)
+{
+    RankPlan rp{};
+    rp.lp = make_layout_plan(T, K, R, 1);
+    rp.lp.key_experts = E;
+    rp.lp.key_div = E / R;
+    rp.off_misc = rp.lp.bytes;
+    rp.bytes = align256(rp.off_misc + 4);
+    return rp;
+}
+
 hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *counts,
                          int32_t *offsets, int32_t *tokens_per_rank, uint8_t *is_token_in_rank,
                          int32_t *num_invalid, char *ws, hipStream_t s)
@@ -408,8 +454,9 @@ hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *
         return hipErrorInvalidValue;     // a chunk's entries must fit its waves
     if (p.nchunk > 0) {
         hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunk), dim3(p.waves * kWave), p.lds, s,
-                           topk_idx, p.T, p.K, p.E, p.R, p.CT, p.nbits, p.epl, hist, rank, rpart,
-                           ipart, is_token_in_rank, counts, offsets, tokens_per_rank, num_invalid);
+                           topk_idx, p.T, p.K, p.E, p.R, p.CT, p.nbits, p.epl, p.key_experts,
+                           p.key_div, hist, rank, rpart, ipart, is_token_in_rank, counts, offsets,
+                           tokens_per_rank, num_invalid);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess)
             return err;

@@ -295,6 +295,91 @@ ep_status_t ep_combine_expert_choice(const uint16_t *y, const float *weights, in
                                      const int32_t *tok_off, const int32_t *tok_ent, int T,
                                      uint16_t *out, void *stream);
 
+/*
+ * One rank's share of the expert-parallel exchange -- [EPA] API Overview:
+ * get_dispatch_layout returns num_tokens_per_rank and is_token_in_rank,
+ * dispatch sends each token to the ranks that hold its experts ("tokens to
+ * expert ranks"), and combine reduces what comes back.  Rank r owns experts
+ * [r*E/R, (r+1)*E/R).  The exchange between ranks is not part of libep:
+ * what a sender packs for rank r is what rank r receives from it, and the
+ * partial sums rank r returns are what the sender adds.
+ *
+ *   sender:    ep_pack_by_rank
+ *   receiver:  the rows it received from the source ranks, concatenated in
+ *              source-rank order, scattered into its E/R experts by
+ *              ep_get_dispatch_layout + ep_dispatch with topk_idx = the
+ *              received send_idx rows and E/R experts: the stable scatter,
+ *              so an expert's rows are in (source rank, source token, k)
+ *              order; then, after the experts, ep_combine_partial with the
+ *              received send_w rows as weights
+ *   sender:    ep_combine_ranks over the returned partial rows
+ */
+
+/* Bytes of device workspace that ep_pack_by_rank needs. */
+size_t ep_pack_workspace_bytes(int T, int K, int E, int R);
+
+/*
+ * ep_pack_by_rank -- the sender's rows, grouped by destination rank: token t
+ * is sent once to each rank r that holds at least one of its valid entries
+ * (is_token_in_rank[t, r] of ep_get_dispatch_layout), as one row of x with
+ * the token's K entries rewritten for r.  Rows are ordered by rank, then by
+ * token (a stable counting sort keyed by (rank, token)):
+ *   tokens_per_rank [R] int32 out: tokens sent to rank r.
+ *   rank_offsets    [R+1] int32 out: exclusive prefix sum of tokens_per_rank;
+ *                   rank r's rows start at rank_offsets[r].
+ *   row of (t, r):  p = rank_offsets[r] + number of tokens t' < t sent to r;
+ *                   kept if p < max_rows (T * min(K, R) always suffices),
+ *                   else counted in num_dropped.  For each kept row:
+ *   send_x   [max_rows, H] bf16 out: send_x[p] = x[t].
+ *   send_src [max_rows] int32 out: t.
+ *   send_idx [max_rows, K] int32 out: for each k, topk_idx[t,k] - r*E/R
+ *            (the local expert id) if entry k is valid and on rank r, else -1.
+ *   send_w   [max_rows, K] fp32 out or NULL: topk_weights[t,k] (1 when
+ *            topk_weights is NULL) where send_idx >= 0, else 0.
+ *   pack_pos [T, R] int32 out: p for kept (t, r) rows, -1 otherwise (the
+ *            handle for ep_combine_ranks).
+ *   num_dropped [1] int32 out.
+ * Rows p >= rank_offsets[R] are not written.  Invalid entries (neither -1
+ * nor in [0, E)) are ignored like -1.
+ *   ws, ws_bytes  workspace of >= ep_pack_workspace_bytes(T, K, E, R) bytes.
+ * Constraints: those of ep_get_dispatch_layout (1 <= R <= 1024, E % R == 0),
+ * H % 8 == 0, max_rows >= 0, T*R and max_rows*K < 2^31.
+ */
+ep_status_t ep_pack_by_rank(const uint16_t *x, int T, int H, const int32_t *topk_idx,
+                            const float *topk_weights, int K, int E, int R, int max_rows,
+                            int32_t *tokens_per_rank, int32_t *rank_offsets, uint16_t *send_x,
+                            int32_t *send_src, int32_t *send_idx, float *send_w,
+                            int32_t *pack_pos, int32_t *num_dropped, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/*
+ * ep_combine_partial -- the receiving rank's combine: ep_combine with fp32
+ * output rows, the partial sums that go back to the sender.
+ *   partial[p, :] = sum over k with slot[p,k] in [0, y_rows) of
+ *                   weights[p,k] * y[slot[p,k], :]
+ * in fp32 (a row with no kept slot gives +0).
+ *   y        [y_rows, H] bf16 in.   slot [S, K] int32 in (from ep_dispatch).
+ *   weights  [S, K] fp32 in (the received send_w), or NULL for unit weights.
+ *   partial  [S, H] fp32 out, 16-byte aligned; must not overlap y.
+ */
+ep_status_t ep_combine_partial(const uint16_t *y, int y_rows, int H, const int32_t *slot,
+                               const float *weights, int S, int K, float *partial, void *stream);
+
+/*
+ * ep_combine_ranks -- the sender's sum after the reverse exchange:
+ *   out[t, :] = bf16( sum over r = 0 .. R-1, in that order, with
+ *                     pack_pos[t, r] in [0, rows), of partial[pack_pos[t,r], :] )
+ * with fp32 adds, rounded once to nearest even; a token no rank received
+ * gives +0.
+ *   partial  [rows, H] fp32 in: the rows the receivers returned, at the
+ *            positions their tokens had in send_x.
+ *   pack_pos [T, R] int32 in (from ep_pack_by_rank).
+ *   out      [T, H] bf16 out; must not overlap partial.
+ * Constraints: 1 <= R <= 1024, H % 8 == 0, T*R < 2^31.
+ */
+ep_status_t ep_combine_ranks(const float *partial, int rows, int H, const int32_t *pack_pos,
+                             int T, int R, uint16_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -124,3 +124,46 @@ def ec_combine(y_d, w_d, off_d, ent_d, T):
 # the combine tolerance (NaN-proof; see tests/tolerance.py)
 bf16_f64 = _tol.bf16_f64
 assert_combine_close = _tol.assert_combine_close
+assert_f32_close = _tol.assert_f32_close
+
+
+# ---------------------------------------------------------------- one rank's share
+def pack_by_rank(x_d, idx_d, w_d, E, R, max_rows=None):
+    """ep_pack_by_rank with sentinel-filled outputs."""
+    T, H = x_d.shape
+    K = idx_d.shape[1]
+    if max_rows is None:
+        max_rows = T * min(K, R)
+    wsb = N.ep_pack_workspace_bytes(T, K, E, R)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    o = dict(tokens_per_rank=torch.full((R,), -7, dtype=torch.int32, device=DEV),
+             rank_offsets=torch.full((R + 1,), -7, dtype=torch.int32, device=DEV),
+             send_x=torch.full((max(max_rows, 1), H), SENT16, dtype=torch.int16,
+                               device=DEV).view(torch.bfloat16),
+             send_src=torch.full((max(max_rows, 1),), -2, dtype=torch.int32, device=DEV),
+             send_idx=torch.full((max(max_rows, 1), K), -3, dtype=torch.int32, device=DEV),
+             send_w=torch.full((max(max_rows, 1), K), -5.0, dtype=torch.float32, device=DEV),
+             pack_pos=torch.full((T, R), -9, dtype=torch.int32, device=DEV),
+             num_dropped=torch.full((1,), -7, dtype=torch.int32, device=DEV))
+    N.ep_pack_by_rank(p(x_d), T, H, p(idx_d), p(w_d), K, E, R, max_rows, p(o["tokens_per_rank"]),
+                      p(o["rank_offsets"]), p(o["send_x"]), p(o["send_src"]), p(o["send_idx"]),
+                      p(o["send_w"]), p(o["pack_pos"]), p(o["num_dropped"]), p(ws), wsb,
+                      stream())
+    o["ws"] = ws
+    return o
+
+
+def combine_partial(y_d, slot_d, w_d):
+    S, K = slot_d.shape
+    H = y_d.shape[1]
+    part = torch.full((S, H), float("nan"), dtype=torch.float32, device=DEV)
+    N.ep_combine_partial(p(y_d), y_d.shape[0], H, p(slot_d), p(w_d), S, K, p(part), stream())
+    return part
+
+
+def combine_ranks(part_d, pos_d):
+    T, R = pos_d.shape
+    H = part_d.shape[1]
+    out = torch.full((T, H), SENT16, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    N.ep_combine_ranks(p(part_d), part_d.shape[0], H, p(pos_d), T, R, p(out), stream())
+    return out

@@ -318,3 +318,67 @@ def test_header_is_plain_c_and_links(tmp_path, std):
     assert r.returncode == 0, r.stdout + r.stderr
     first = r.stdout.split()
     assert first[0] != "0" and "workspace" in r.stdout and first[-1] == "14"
+
+
+def _pack(**kw):
+    args = dict(x=A, T=16, H=256, topk_idx=A, topk_weights=A, K=2, E=8, R=4, max_rows=32,
+                tokens_per_rank=A, rank_offsets=A, send_x=B, send_src=A, send_idx=A, send_w=A,
+                pack_pos=A, num_dropped=A, ws=WS, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return N.ep_pack_by_rank(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=0), N.EP_ERR_INVALID_ARG),
+    (dict(E=8, R=3), N.EP_ERR_INVALID_ARG),
+    (dict(R=2048, E=2048), N.EP_ERR_UNSUPPORTED),
+    (dict(H=12), N.EP_ERR_INVALID_ARG),
+    (dict(max_rows=-1), N.EP_ERR_INVALID_ARG),
+    (dict(tokens_per_rank=None), N.EP_ERR_INVALID_ARG),
+    (dict(rank_offsets=None), N.EP_ERR_INVALID_ARG),
+    (dict(pack_pos=None), N.EP_ERR_INVALID_ARG),
+    (dict(send_x=None), N.EP_ERR_INVALID_ARG),
+    (dict(send_idx=None), N.EP_ERR_INVALID_ARG),
+    (dict(x=A + 8), N.EP_ERR_INVALID_ARG),
+    (dict(send_w=A + 2), N.EP_ERR_INVALID_ARG),
+    (dict(H=(1 << 24) + 8), N.EP_ERR_UNSUPPORTED),
+    (dict(ws=None), N.EP_ERR_WORKSPACE),
+    (dict(ws_bytes=64), N.EP_ERR_WORKSPACE),
+])
+def test_pack_rejects(kw, status):
+    assert _pack(**kw) == status
+
+
+def test_pack_workspace_bytes():
+    assert N.ep_pack_workspace_bytes(4096, 8, 256, 8) >= 4096 * 8 * 4
+    assert N.ep_pack_workspace_bytes(4096, 8, 256, 3) == 0
+    assert N.ep_pack_workspace_bytes(0, 8, 256, 8) > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=-1), N.EP_ERR_INVALID_ARG),
+    (dict(K=0), N.EP_ERR_INVALID_ARG),
+    (dict(H=12), N.EP_ERR_INVALID_ARG),
+    (dict(partial=A + 4), N.EP_ERR_INVALID_ARG),
+    (dict(partial=None), N.EP_ERR_INVALID_ARG),
+    (dict(y=None), N.EP_ERR_INVALID_ARG),
+])
+def test_combine_partial_rejects(kw, status):
+    args = dict(y=A, y_rows=64, H=256, slot=A, weights=A, S=16, K=2, partial=B, stream=None)
+    args.update(kw)
+    assert N.ep_combine_partial(**args, check=False) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(R=0), N.EP_ERR_INVALID_ARG),
+    (dict(R=2048), N.EP_ERR_UNSUPPORTED),
+    (dict(T=-1), N.EP_ERR_INVALID_ARG),
+    (dict(H=4), N.EP_ERR_INVALID_ARG),
+    (dict(pack_pos=None), N.EP_ERR_INVALID_ARG),
+    (dict(out=A + 8), N.EP_ERR_INVALID_ARG),
+    (dict(partial=None), N.EP_ERR_INVALID_ARG),
+])
+def test_combine_ranks_rejects(kw, status):
+    args = dict(partial=A, rows=64, H=256, pack_pos=A, T=16, R=4, out=B, stream=None)
+    args.update(kw)
+    assert N.ep_combine_ranks(**args, check=False) == status

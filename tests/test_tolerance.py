@@ -61,3 +61,23 @@ def test_bound_edges():
 def test_shape_mismatch_fails():
     with pytest.raises(AssertionError):
         T.assert_combine_close(REF[:3], REF)
+
+
+@pytest.mark.parametrize("planted", [np.nan, -np.nan, np.inf, -np.inf])
+def test_f32_non_finite_fails(planted):
+    ref = np.array([1.0, -2.5, 0.0, 384.0], np.float32)
+    T.assert_f32_close(ref.copy(), ref)
+    for where in range(4):
+        got = ref.copy()
+        got[where] = planted
+        with pytest.raises(AssertionError):
+            T.assert_f32_close(got, ref)
+
+
+def test_f32_bound_edges():
+    ref = np.array([384.0, 0.0], np.float32)
+    T.assert_f32_close(np.array([386.9, 0.00099], np.float32), ref)
+    with pytest.raises(AssertionError):
+        T.assert_f32_close(np.array([387.1, 0.0], np.float32), ref)
+    with pytest.raises(AssertionError):
+        T.assert_f32_close(np.array([384.0, 0.0011], np.float32), ref)

@@ -35,3 +35,23 @@ def assert_combine_close(got_bits, ref_bits, what=""):
         raise AssertionError((what, int(bad[0].size),
                               [(tuple(int(i) for i in ix), g[ix], r[ix])
                                for ix in list(zip(*bad))[:5]]))
+
+
+def f32_bad(got, ref):
+    """The same bound on fp32 values (the partial sums of the exchange)."""
+    g = np.asarray(got, np.float32).astype(np.float64)
+    r = np.asarray(ref, np.float32).astype(np.float64)
+    if g.shape != r.shape:
+        raise AssertionError(f"shape {g.shape} against {r.shape}")
+    with np.errstate(invalid="ignore", over="ignore"):
+        ok = np.abs(g - r) <= REL * np.abs(r) + ABS
+    return np.nonzero(~ok)
+
+
+def assert_f32_close(got, ref, what=""):
+    bad = f32_bad(got, ref)
+    if bad[0].size:
+        g, r = np.asarray(got), np.asarray(ref)
+        raise AssertionError((what, int(bad[0].size),
+                              [(tuple(int(i) for i in ix), g[ix], r[ix])
+                               for ix in list(zip(*bad))[:5]]))
