@@ -125,9 +125,10 @@ def trace_avg_us(key, kernel):
     return None if k is None else k.get("avg_us")
 
 
-def workload_key(c, meta, chunk, two_call):
+def workload_key(c, meta, chunk, two_call, ranks=0):
     """Name of a bench configuration: the workload, plus the dispatch mode
-    when it is not the workload's own, the round size and the decode form."""
+    when it is not the workload's own, the round size, the decode form and
+    the rank count of the exchange share."""
     key = c.name
     if meta.get("quant") is not None and meta["quant"] != getattr(c, "default_quant", None):
         key += "_" + meta["quant"]
@@ -135,6 +136,8 @@ def workload_key(c, meta, chunk, two_call):
         key += f"_chunk{chunk}"
     if two_call:
         key += "_two_call"
+    if ranks:
+        key += f"_ranks{ranks}"
     return key
 
 
@@ -378,6 +381,95 @@ def low_latency_path(c, N, torch, dev, sp):
                          "out": out})
 
 
+def ranks_path(c, N, torch, dev, sp, R):
+    """One rank's share of the expert-parallel exchange with R ranks, as one
+    GPU runs it: ep_pack_by_rank sends the T local tokens once per rank that
+    holds one of their experts; the receiver takes the R blocks, concatenated
+    in rank order as one rank receives R sources' blocks, and scatters them
+    into its E/R experts (ep_get_dispatch_layout + ep_dispatch on the local
+    ids); identity experts; ep_combine_partial makes the fp32 partial sums;
+    ep_combine_ranks adds them per token in rank order.  The exchange itself
+    (between GPUs) is not part of the step."""
+    T, H, E, K = c.T, c.H, c.E, c.K
+    if c.quant != "bf16" or E % R:
+        raise SystemExit("--ranks needs a bf16 token-choice workload with E % R == 0")
+    per = E // R
+    P = lambda t: t.data_ptr() if t is not None else None
+    x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    idx = torch.from_numpy(c.topk_idx).to(dev)
+    w = torch.from_numpy(c.topk_weights).to(dev)
+    # buffer sizes from the routing, as the count exchange tells a rank
+    valid = (c.topk_idx >= 0) & (c.topk_idx < E)
+    rank_of = np.where(valid, c.topk_idx // per, -1)
+    S = int(sum(len(set(row[row >= 0].tolist())) for row in rank_of))
+    n_valid = int(valid.sum())
+    pws_bytes = N.ep_pack_workspace_bytes(T, K, E, R)
+    pws = torch.empty(pws_bytes, dtype=torch.uint8, device=dev)
+    tpr = torch.empty(R, dtype=torch.int32, device=dev)
+    roff = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    send_x = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+    send_src = torch.empty(S, dtype=torch.int32, device=dev)
+    send_idx = torch.empty((S, K), dtype=torch.int32, device=dev)
+    send_w = torch.empty((S, K), dtype=torch.float32, device=dev)
+    pos = torch.empty((T, R), dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    rws_bytes = N.ep_workspace_bytes(S, K, per, 1)
+    rws = torch.empty(rws_bytes, dtype=torch.uint8, device=dev)
+    counts = torch.empty(per, dtype=torch.int32, device=dev)
+    offsets = torch.empty(per + 1, dtype=torch.int32, device=dev)
+    tpr1 = torch.empty(1, dtype=torch.int32, device=dev)
+    itr = torch.empty((S, 1), dtype=torch.uint8, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    recv = torch.empty((n_valid, H), dtype=torch.bfloat16, device=dev)
+    slot = torch.empty((S, K), dtype=torch.int32, device=dev)
+    src = torch.empty(n_valid, dtype=torch.int32, device=dev)
+    nd_r = torch.empty(1, dtype=torch.int32, device=dev)
+    part = torch.empty((S, H), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def pack():
+        N.ep_pack_by_rank(P(x), T, H, P(idx), P(w), K, E, R, S, P(tpr), P(roff), P(send_x),
+                          P(send_src), P(send_idx), P(send_w), P(pos), P(nd), P(pws), pws_bytes,
+                          sp)
+
+    def layout():
+        N.ep_get_dispatch_layout(P(send_idx), S, K, per, 1, P(counts), P(offsets), P(tpr1),
+                                 P(itr), P(ninv), P(rws), rws_bytes, sp)
+
+    def dispatch():
+        N.ep_dispatch(P(send_x), S, H, P(send_idx), K, per, P(offsets), N.EP_LAYOUT_CONTIGUOUS,
+                      n_valid, N.EP_QUANT_BF16, P(recv), None, P(slot), P(src), P(nd_r), P(rws),
+                      rws_bytes, sp)
+
+    def partial():
+        N.ep_combine_partial(P(recv), n_valid, H, P(slot), P(send_w), S, K, P(part), sp)
+
+    def rank_sum():
+        N.ep_combine_ranks(P(part), S, H, P(pos), T, R, P(out), sp)
+
+    meta_b = 2 * S * K * 4
+    alg = {"pack": T * H * 2 + 2 * T * K * 4 + S * H * 2 + S * 4 + 2 * S * K * 4 + T * R * 4,
+           "layout": S * K * 4,
+           "dispatch": S * H * 2 + n_valid * H * 2 + meta_b,
+           "partial": n_valid * H * 2 + S * H * 4 + meta_b,
+           "rank_sum": S * H * 4 + T * H * 2 + T * R * 4}
+    kern = {"pack": "rank_pack_kernel", "layout": "layout_chunk_kernel",
+            "dispatch": "dispatch_kernel", "partial": "combine_kernel",
+            "rank_sum": "rank_sum_kernel"}
+    meta = {"T": T, "H": H, "E": E, "top_k": K, "ranks": R, "experts_per_rank": per,
+            "quant": "bf16", "recv_layout": "contiguous", "combine": "weighted",
+            "valid_slots": n_valid, "packed_rows": S,
+            "step": "pack -> receiver layout + scatter (E/R local experts) -> partial combine "
+                    "(fp32) -> rank sum; identity experts, no inter-GPU exchange"}
+    return Path(c.name, T, [("pack", pack), ("layout", layout), ("dispatch", dispatch),
+                            ("partial", partial), ("rank_sum", rank_sum)], kern, alg, meta,
+                kind="ranks",
+                outputs={"tokens_per_rank": tpr, "rank_offsets": roff, "send_x": send_x,
+                         "send_src": send_src, "send_idx": send_idx, "send_w": send_w,
+                         "pack_pos": pos, "num_dropped": nd, "slot": slot, "recv": recv,
+                         "partial": part, "out": out, "R": R})
+
+
 def expert_choice_path(c, N, torch, dev, sp):
     T, H, E, C = c.T, c.H, c.E, c.C
     P = lambda t: t.data_ptr()
@@ -435,6 +527,14 @@ def _combine_bad(got_bits, ref_bits):
     f = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32) \
         .astype(np.float64)
     g, r = f(got_bits), f(ref_bits)
+    with np.errstate(invalid="ignore", over="ignore"):
+        return int(np.count_nonzero(~(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-3)))
+
+
+def _combine_bad_f32(got, ref):
+    """The same bound on fp32 values."""
+    g = np.asarray(got, np.float32).astype(np.float64)
+    r = np.asarray(ref, np.float32).astype(np.float64)
     with np.errstate(invalid="ignore", over="ignore"):
         return int(np.count_nonzero(~(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-3)))
 
@@ -508,6 +608,30 @@ def _check_chunked(oracle, c, path, g, ck):
     return f"chunked: last round's slots, {T} combined tokens against the unchunked oracle"
 
 
+def _check_ranks(oracle, c, path, g, ck):
+    R = g["R"]
+    E, K, T = c.E, c.K, c.T
+    per = E // R
+    S = path.meta["packed_rows"]
+    ref = oracle.rank_pack(c.x, c.topk_idx, c.topk_weights, E, R, S)
+    ck.equal("rank_offsets", g["rank_offsets"], ref["rank_offsets"])
+    ck.equal("tokens_per_rank", g["tokens_per_rank"], np.diff(ref["rank_offsets"]).astype(np.int32))
+    ck.equal("pack_pos", g["pack_pos"], ref["pack_pos"])
+    ck.equal("num_dropped", g["num_dropped"], np.array([ref["num_dropped"]], np.int32))
+    for k in ("send_x", "send_src", "send_idx", "send_w"):
+        ck.equal(k, g[k], ref[k][:S])
+    rows = path.meta["valid_slots"]
+    s_ref, _, _ = oracle.slots(ref["send_idx"][:S], per, False, rows)
+    ck.equal("receive slots", g["slot"], s_ref)
+    y = oracle.dispatch_bf16(ref["send_x"][:S], s_ref, rows)
+    ck.equal("received rows", g["recv"], y)
+    part = oracle.combine_partial(y, s_ref, ref["send_w"][:S])
+    bad = _combine_bad_f32(g["partial"], part)
+    (ck.done if bad == 0 else ck.failed).append("partial" if bad == 0 else f"partial ({bad})")
+    ck.close("rank sum", g["out"], oracle.combine_ranks(part, ref["pack_pos"]))
+    return f"ranks R={R}: {S} packed rows, {rows} received rows, {T} combined tokens"
+
+
 def _check_expert_choice(oracle, c, path, g, ck):
     recv, ninv = oracle.ec_dispatch(c.x, c.token_indices)
     off, ent = oracle.ec_invert(c.token_indices, c.T)
@@ -523,8 +647,18 @@ def _check_expert_choice(oracle, c, path, g, ck):
     return f"expert choice: {int(keep.sum())} receive rows, inverse map, {c.T} combined tokens"
 
 
-def _oracle_pass(oracle, c):
+def _oracle_pass(oracle, c, R=0):
     """One full pass of the workload through the oracle."""
+    if R:
+        per = c.E // R
+        pk = oracle.rank_pack(c.x, c.topk_idx, c.topk_weights, c.E, R)
+        S = int(pk["rank_offsets"][R])
+        rows = int((pk["send_idx"][:S] >= 0).sum())
+        s, _, _ = oracle.slots(pk["send_idx"][:S], per, False, rows)
+        y = oracle.dispatch_bf16(pk["send_x"][:S], s, rows)
+        part = oracle.combine_partial(y, s, pk["send_w"][:S])
+        oracle.combine_ranks(part, pk["pack_pos"])
+        return f"rank pack (R={R}), receiver slots and scatter, partial combine, rank sum"
     if hasattr(c, "token_indices"):
         recv, _ = oracle.ec_dispatch(c.x, c.token_indices)
         oracle.ec_invert(c.token_indices, c.T)
@@ -544,11 +678,11 @@ def _oracle_pass(oracle, c):
     return "layout, slots, dispatch, weighted combine"
 
 
-def _time_oracle(oracle, c, budget_s):
+def _time_oracle(oracle, c, budget_s, R=0):
     reps = 0
     t0 = time.perf_counter()
     while True:
-        what = _oracle_pass(oracle, c)
+        what = _oracle_pass(oracle, c, R)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -565,8 +699,11 @@ def cpu_baseline(c, path, g, budget_s, torch):
     cores.  Returns (parity, cpu_baseline, cpu_baseline_all_cores)."""
     import oracle
     ck = _Checks()
+    R = g.get("R", 0) if path.kind == "ranks" else 0
     if path.kind == "expert_choice":
         what = _check_expert_choice(oracle, c, path, g, ck)
+    elif path.kind == "ranks":
+        what = _check_ranks(oracle, c, path, g, ck)
     elif path.kind == "chunked":
         what = _check_chunked(oracle, c, path, g, ck)
     else:
@@ -576,12 +713,12 @@ def cpu_baseline(c, path, g, budget_s, torch):
     if budget_s <= 0:
         return parity, None, None
     host = {"host_cpu": host_cpu_model(), "host_logical_cpus": os.cpu_count()}
-    reps, el, what = _time_oracle(oracle, c, budget_s)
+    reps, el, what = _time_oracle(oracle, c, budget_s, R)
     one = {"value": reps * c.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
            "sample": f"{reps} full pass(es) of the same workload ({what}; {c.T} tokens each), "
                      f"{el:.1f} s on one host thread", **host}
     with oracle.all_cores() as threads:
-        reps, el, what = _time_oracle(oracle, c, budget_s)
+        reps, el, what = _time_oracle(oracle, c, budget_s, R)
     allc = {"value": reps * c.T / el, "unit": "tokens/s", "cores": threads,
             "kind": "oracle (-fopenmp build: token-major loops parallel, layout and slots "
                     "serial)",
@@ -622,6 +759,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=0,
                     help="run a token-choice step in rounds of at most this many tokens "
                          "(0 = one round)")
+    ap.add_argument("--ranks", type=int, default=0,
+                    help="one rank's share of the expert-parallel exchange with this many "
+                         "ranks: pack, receiver scatter, partial combine, rank sum (0 = off)")
     ap.add_argument("--two-call", action="store_true",
                     help="decode: ep_get_dispatch_layout + ep_dispatch (padded) instead of "
                          "the one-launch ep_low_latency_dispatch")
@@ -658,6 +798,8 @@ def main():
         c.quant = a.quant
     if a.workload == "expert_choice":
         path = expert_choice_path(c, N, torch, dev, sp)
+    elif a.ranks > 0:
+        path = ranks_path(c, N, torch, dev, sp, a.ranks)
     elif a.chunk > 0:
         path = chunked_token_choice_path(c, N, torch, dev, sp, a.chunk)
     elif a.workload == "decode" and not a.two_call:
@@ -742,18 +884,20 @@ def main():
                 "achieved_GBps": sum(path.alg_bytes.values()) / (med * 1e-6) / 1e9}
 
     alg_total = sum(path.alg_bytes.values())
-    dom = max(("dispatch", "combine"), key=lambda n: op_us[n])
+    dom = max((n for n in op_us if n != "layout"), key=lambda n: op_us[n])
     dom_us, dom_bytes = op_us[dom] / launches[dom], path.alg_bytes[dom] / launches[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     headline = (a.workload == "prefill" and path.meta.get("quant") == "bf16"
-                and "chunk_tokens" not in path.meta)
-    key = workload_key(c, path.meta, a.chunk, a.two_call and a.workload == "decode")
+                and "chunk_tokens" not in path.meta and "ranks" not in path.meta)
+    key = workload_key(c, path.meta, a.chunk, a.two_call and a.workload == "decode", a.ranks)
     res = {
         "metric": HEADLINE_METRIC if headline else
                   f"dispatch+combine tokens/s & achieved HBM GB/s, {c.name}"
                   + (f" ({path.meta['quant']})" if path.meta.get("quant", "bf16") != "bf16" else "")
                   + (f" (rounds of {path.meta['chunk_tokens']} tokens)"
-                     if "chunk_tokens" in path.meta else ""),
+                     if "chunk_tokens" in path.meta else "")
+                  + (f" (one rank's share of the exchange, R={path.meta['ranks']})"
+                     if "ranks" in path.meta else ""),
         "value": path.T / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -772,6 +916,8 @@ def main():
         "algorithmic_bytes_per_step": alg_total,
         "algorithmic_bytes_per_op": path.alg_bytes,
         "timed_region_event_ms_per_step": region_ms,
+        "per_op_GBps": {n: path.alg_bytes[n] / launches[n] / (op_us[n] / launches[n] * 1e-6) / 1e9
+                        for n in op_us},
         "per_op_us": {**op_us, "step_with_op_events": float(step_ev.mean()),
                       "step_with_op_events_p10": float(np.percentile(step_ev, 10)),
                       "step_with_op_events_p90": float(np.percentile(step_ev, 90))},
