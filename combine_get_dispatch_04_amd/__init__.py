@@ -2,18 +2,22 @@
 
 `_native` is the ctypes binding of libep.so with the C ABI's names
 (ep_get_dispatch_layout, ep_dispatch, ep_combine, ep_dispatch_expert_choice,
-ep_combine_expert_choice); `api` is a torch-tensor front end over it.
+ep_combine_expert_choice, and one rank's share of the exchange:
+ep_pack_by_rank, ep_combine_partial, ep_combine_ranks); `api` is a
+torch-tensor front end over it.
 `workloads` makes the seeded synthetic inputs.  The library is loaded on
 first use and a missing build raises instead of falling back.
 """
 from . import _native
-from ._native import (EpError, ep_combine, ep_combine_expert_choice, ep_dispatch,
-                      ep_dispatch_expert_choice, ep_ec_workspace_bytes, ep_get_dispatch_layout,
-                      ep_workspace_bytes)
+from ._native import (EpError, ep_combine, ep_combine_expert_choice, ep_combine_partial,
+                      ep_combine_ranks, ep_dispatch, ep_dispatch_expert_choice,
+                      ep_ec_workspace_bytes, ep_get_dispatch_layout, ep_pack_by_rank,
+                      ep_pack_workspace_bytes, ep_workspace_bytes)
 
 __all__ = ["EpError", "ep_get_dispatch_layout", "ep_dispatch", "ep_combine",
-           "ep_dispatch_expert_choice", "ep_combine_expert_choice", "ep_workspace_bytes",
-           "ep_ec_workspace_bytes", "api", "workloads"]
+           "ep_dispatch_expert_choice", "ep_combine_expert_choice", "ep_pack_by_rank",
+           "ep_combine_partial", "ep_combine_ranks", "ep_workspace_bytes",
+           "ep_ec_workspace_bytes", "ep_pack_workspace_bytes", "api", "workloads"]
 
 
 def __getattr__(name):

@@ -354,3 +354,115 @@ def combine_expert_choice(y: torch.Tensor, handle: ExpertChoiceHandle,
         N.ep_combine_expert_choice(_ptr(y), _ptr(handle.weights), E, C, H, _ptr(handle.tok_off),
                                    _ptr(handle.tok_ent), T, _ptr(out), _stream(dev))
     return out
+
+
+# ---------------------------------------------------------------- one rank's share
+@dataclass
+class RankPack:
+    """What the sender packs ("DeepEP-Ascend" README, API Overview: the
+    dispatch sends each token to the ranks of its experts): rows grouped by
+    destination rank, each token once per rank that holds one of its
+    experts, with that rank's local expert ids."""
+    num_tokens_per_rank: torch.Tensor          # [R] int32
+    rank_offsets: torch.Tensor                 # [R+1] int32: rank r's rows start here
+    send_x: torch.Tensor                       # [rows, H] bf16
+    send_src: torch.Tensor                     # [rows] int32: source token
+    send_idx: torch.Tensor                     # [rows, K] int32: local expert ids, -1 elsewhere
+    send_w: torch.Tensor                       # [rows, K] float32: weights, 0 where send_idx is -1
+    pack_pos: torch.Tensor                     # [T, R] int32: row of (t, r) or -1
+    num_dropped: torch.Tensor                  # [1] int32
+    num_ranks: int
+    experts_per_rank: int
+
+
+def pack_by_rank(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                 topk_weights: Optional[torch.Tensor] = None,
+                 max_rows: Optional[int] = None) -> RankPack:
+    """The sender's rows for R ranks (rank r owns experts [r E/R, (r+1) E/R)):
+    rows ordered by rank, then token.  `max_rows` defaults to T * min(K, R),
+    always enough; rows beyond it are dropped and counted."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    T, H = x.shape
+    if topk_idx.shape[0] != T:
+        raise ValueError("x and topk_idx disagree on the number of tokens")
+    K = topk_idx.shape[1]
+    E, R = int(num_experts), int(num_ranks)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, 2)
+        if tuple(topk_weights.shape) != (T, K):
+            raise ValueError("topk_weights must be [T, K]")
+    dev = x.device
+    _same_device(dev, topk_idx=topk_idx, topk_weights=topk_weights)
+    rows = T * min(K, R) if max_rows is None else int(max_rows)
+    ws_bytes = N.ep_pack_workspace_bytes(T, K, E, R)
+    if ws_bytes == 0:
+        raise N.EpError("ep_pack_workspace_bytes", N.EP_ERR_INVALID_ARG)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    tpr = torch.empty(R, dtype=torch.int32, device=dev)
+    off = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    sx = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    src = torch.empty(rows, dtype=torch.int32, device=dev)
+    sidx = torch.empty((rows, K), dtype=torch.int32, device=dev)
+    sw = torch.empty((rows, K), dtype=torch.float32, device=dev)
+    pos = torch.empty((T, R), dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        N.ep_pack_by_rank(_ptr(x), T, H, _ptr(topk_idx), _ptr(topk_weights), K, E, R, rows,
+                          _ptr(tpr), _ptr(off), _ptr(sx), _ptr(src), _ptr(sidx), _ptr(sw),
+                          _ptr(pos), _ptr(nd), _ptr(ws), ws_bytes, _stream(dev))
+    return RankPack(tpr, off, sx, src, sidx, sw, pos, nd, R, E // R)
+
+
+def receive(recv_x: torch.Tensor, recv_idx: torch.Tensor, experts_per_rank: int, *,
+            quant: str = "bf16", max_rows: Optional[int] = None):
+    """The receiving rank's scatter of the rows it received (the blocks of
+    its source ranks, concatenated in rank order) into its local experts:
+    the layout and the stable scatter with the received local ids as
+    topk_idx, so an expert's rows are in (source rank, source token, k)
+    order.  -> (Layout, recv, recv_scales or None, Handle)."""
+    layout = get_dispatch_layout(recv_idx, experts_per_rank)
+    recv, scales, handle = dispatch(recv_x, layout, quant=quant, max_rows=max_rows)
+    return layout, recv, scales, handle
+
+
+def combine_partial(y: torch.Tensor, handle: Handle, weights: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The receiving rank's combine: per received row, sum_k w * y[slot] in
+    fp32, kept in fp32 for the sender (the partial sums of the exchange)."""
+    _need(y, "y", torch.bfloat16, 2)
+    S, K = handle.slot.shape
+    H = y.shape[1]
+    if weights is not None:
+        _need(weights, "weights", torch.float32, 2)
+        if tuple(weights.shape) != (S, K):
+            raise ValueError("weights must be [rows, K]")
+    dev = y.device
+    _same_device(dev, slot=handle.slot, weights=weights)
+    if out is None:
+        out = torch.empty((S, H), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", torch.float32, 2)
+        if tuple(out.shape) != (S, H):
+            raise ValueError(f"out must be {(S, H)}, got {tuple(out.shape)}")
+        _same_device(dev, out=out)
+    with torch.cuda.device(dev):
+        N.ep_combine_partial(_ptr(y), y.shape[0], H, _ptr(handle.slot), _ptr(weights), S, K,
+                             _ptr(out), _stream(dev))
+    return out
+
+
+def combine_ranks(partial: torch.Tensor, pack: RankPack,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The sender's sum of the partial rows the ranks returned (at the rows
+    their tokens had in send_x), in rank order, rounded once to bf16."""
+    _need(partial, "partial", torch.float32, 2)
+    T, R = pack.pack_pos.shape
+    H = partial.shape[1]
+    dev = partial.device
+    _same_device(dev, pack_pos=pack.pack_pos)
+    out = _out(out, (T, H), dev)
+    with torch.cuda.device(dev):
+        N.ep_combine_ranks(_ptr(partial), partial.shape[0], H, _ptr(pack.pack_pos), T, R,
+                           _ptr(out), _stream(dev))
+    return out

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import brute
 import gpu_util as G
 import oracle
 from combine_get_dispatch_04_amd import api
@@ -201,3 +202,57 @@ def test_low_latency_pair(quant):
     G.assert_combine_close(G.host(out), oracle.combine(y, s_ref, c.topk_weights))
     with pytest.raises(ValueError, match="handle"):
         api.low_latency_combine(y_d, idx[:, :2].contiguous(), w, h)
+
+
+def test_rank_share_through_the_front_end():
+    """pack_by_rank -> receive (the receiver's scatter with E/R experts) ->
+    identity experts -> combine_partial -> combine_ranks, against the oracle
+    at every step; then the same with unit weights, exactly bf16(m x)."""
+    c, x, idx, w = _tc(40, T=500, H=256, E=32, K=6)
+    R = 4
+    per = c.E // R
+    pk = api.pack_by_rank(x, idx, c.E, R, topk_weights=w)
+    torch.cuda.synchronize()
+    ref = oracle.rank_pack(c.x, c.topk_idx, c.topk_weights, c.E, R)
+    S = int(ref["rank_offsets"][R])
+    assert np.array_equal(G.host(pk.rank_offsets), ref["rank_offsets"])
+    assert np.array_equal(G.host(pk.num_tokens_per_rank), np.diff(ref["rank_offsets"]))
+    assert np.array_equal(G.host(pk.pack_pos), ref["pack_pos"])
+    assert np.array_equal(G.host(pk.send_x[:S]), ref["send_x"][:S])
+    assert np.array_equal(G.host(pk.send_idx[:S]), ref["send_idx"][:S])
+    assert np.array_equal(G.host(pk.send_w[:S]), ref["send_w"][:S])
+    assert int(G.host(pk.num_dropped)[0]) == 0 and pk.experts_per_rank == per
+    L, recv, scales, h = api.receive(pk.send_x[:S].contiguous(), pk.send_idx[:S].contiguous(), per)
+    part = api.combine_partial(recv, h, pk.send_w[:S].contiguous())
+    out = api.combine_ranks(part, pk)
+    torch.cuda.synchronize()
+    s_ref, _, _ = oracle.slots(ref["send_idx"][:S], per, False, S * c.K)
+    assert scales is None and np.array_equal(G.host(h.slot), s_ref)
+    y = oracle.dispatch_bf16(ref["send_x"][:S], s_ref, S * c.K)
+    part_ref = oracle.combine_partial(y, s_ref, ref["send_w"][:S])
+    G.assert_f32_close(G.host(part), part_ref)
+    G.assert_combine_close(G.host(out), oracle.combine_ranks(part_ref, ref["pack_pos"]))
+    # unit weights: the pack sends ones, the round trip is exact
+    pk1 = api.pack_by_rank(x, idx, c.E, R)
+    _, recv1, _, h1 = api.receive(pk1.send_x[:S].contiguous(), pk1.send_idx[:S].contiguous(), per)
+    out1 = api.combine_ranks(api.combine_partial(recv1, h1, pk1.send_w[:S].contiguous()), pk1)
+    torch.cuda.synchronize()
+    m = ((c.topk_idx >= 0) & (c.topk_idx < c.E)).sum(axis=1)
+    assert np.array_equal(G.host(out1), brute.multiplicity_times_x(c.x, m))
+
+
+def test_rank_share_argument_checks():
+    c, x, idx, w = _tc(41, T=50, H=64, E=8, K=3)
+    with pytest.raises(ValueError):
+        api.pack_by_rank(x, idx, c.E, 3)                      # E % R != 0
+    with pytest.raises(ValueError):
+        api.pack_by_rank(x[:10], idx, c.E, 4)                 # token counts disagree
+    with pytest.raises(ValueError):
+        api.pack_by_rank(x, idx, c.E, 4, topk_weights=w[:, :2].contiguous())
+    pk = api.pack_by_rank(x, idx, c.E, 4)
+    with pytest.raises(ValueError):
+        api.combine_ranks(torch.zeros((4, 64), dtype=torch.bfloat16, device=G.DEV), pk)
+    _, recv, _, h = api.receive(pk.send_x, pk.send_idx, 2)
+    with pytest.raises(ValueError):
+        api.combine_partial(recv, h, torch.ones((3, 3), dtype=torch.float32, device=G.DEV))
+    torch.cuda.synchronize()
