@@ -918,6 +918,17 @@ def main():
         "timed_region_event_ms_per_step": region_ms,
         "per_op_GBps": {n: path.alg_bytes[n] / launches[n] / (op_us[n] / launches[n] * 1e-6) / 1e9
                         for n in op_us},
+        # every operation against the same roofline: its main kernel, the
+        # algorithmic bytes of one launch, the event-bracketed duration, the
+        # fraction of 8 TB/s and the counter traffic when a summary is current
+        "per_op_roofline": {
+            n: {"kernel": path.kernel_of[n],
+                "algorithmic_bytes_per_launch": path.alg_bytes[n] / launches[n],
+                "avg_launch_us": op_us[n] / launches[n],
+                "frac": path.alg_bytes[n] / (op_us[n] * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                "traffic": traffic_entry(key, path.kernel_of[n]),
+                "rocprof_avg_us": trace_avg_us(key, path.kernel_of[n])}
+            for n in op_us},
         "per_op_us": {**op_us, "step_with_op_events": float(step_ev.mean()),
                       "step_with_op_events_p10": float(np.percentile(step_ev, 10)),
                       "step_with_op_events_p90": float(np.percentile(step_ev, 90))},
