@@ -278,12 +278,20 @@ hipError_t launch_combine_t(const uint16_t *y, int y_rows, int H, const int32_t 
     // and 4 rows requested per round.  Measured on T=16384, K=16 (3.2 GB of
     // rows): 683 -> 641 us; on T=128, K=8: 10.2 -> 9.2 us.  At K = 8 and
     // T = 4096 that shape was 4 us slower than 7 pieces per thread, one row
-    // per round.
+    // per round.  Few tokens with K < 12 (decode): one piece per thread and
+    // 8 rows per round, so a token's K = 8 rows are one round trip (decode
+    // combine 7.0-7.1 -> 6.75 us by events, in two runs each).
     const bool many = K >= 12 || T < 1024;
-    RowShape rs = row_shape(H / 8, many ? 2 : 8);
+    const bool few = T < 1024 && K < 12;
+    RowShape rs = row_shape(H / 8, few ? 1 : (many ? 2 : 8));
     if ((uint64_t)T * rs.bd > 0xFFFFFFFFull)      // work-items per grid dimension fit 32 bits
         return hipErrorInvalidConfiguration;
     dim3 grid(T, rs.nseg), block(rs.bd);
+    if (few) {
+        hipLaunchKernelGGL((combine_kernel<1, 8, F32>), grid, block, 0, s, y, y_rows, H, slot, w,
+                           K, out);
+        return hipGetLastError();
+    }
 #define EP_COMBINE_CASE(N)                                                                       \
     case N:                                                                                      \
         hipLaunchKernelGGL((combine_kernel<N, 1, F32>), grid, block, 0, s, y, y_rows, H, slot, w, \
