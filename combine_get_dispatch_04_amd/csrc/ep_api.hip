@@ -14,7 +14,6 @@ namespace {
 
 constexpr int kMaxExperts = 4096;   // the layout keeps per-expert counts in LDS
 constexpr int kMaxRanks = 1024;
-constexpr int kMaxTopk = 1024;      // a chunk of the layout holds at least one token's row
 constexpr int64_t kI32 = 2147483647LL;
 constexpr int kMaxHidden = 1 << 24; // row byte counts and offsets stay 32-bit in the kernels
 
@@ -26,7 +25,7 @@ ep_status_t check_layout_sizes(int T, int K, int E, int R)
 {
     if (T < 0 || K < 1 || E < 1 || R < 1)
         return EP_ERR_INVALID_ARG;
-    if (E > kMaxExperts || R > kMaxRanks || K > kMaxTopk)
+    if (E > kMaxExperts || R > kMaxRanks)
         return EP_ERR_UNSUPPORTED;
     if (E % R != 0)
         return EP_ERR_INVALID_ARG;

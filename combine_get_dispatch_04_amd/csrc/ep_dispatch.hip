@@ -311,7 +311,7 @@ __device__ __forceinline__ void store_unit(rsrc_t dst, int i, int units, int H, 
 template <int PPT, int MODE, int U, bool LL>
 __global__ void __launch_bounds__(256)
 dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict__ topk_idx, int K,
-                int E, const int32_t *__restrict__ offsets, int padded, int cap_or_rows, int CT,
+                int E, const int32_t *__restrict__ offsets, int padded, int cap_or_rows, int CT, int CE,
                 int nchunk, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ local_rank,
                 void *__restrict__ recv_x, void *__restrict__ recv_s,
                 int32_t *__restrict__ slot_out, int32_t *__restrict__ recv_src,
@@ -445,10 +445,13 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
             const int e = LL ? ll_lds[t * K + k] : trow[k];   // LL: staged with the rest
             if ((unsigned)e < (unsigned)E) {
                 int r;
-                if constexpr (LL)
+                if constexpr (LL) {
                     r = ll_rank;                       // k == lane: K <= 64
-                else
-                    r = chunk_base[(int64_t)e * nchunk + c] + rrow[k];
+                } else {
+                    // rows longer than a layout chunk: each entry's own chunk
+                    const int ck = CE > 0 ? (int)(((int64_t)t * K + k) / CE) : c;
+                    r = chunk_base[(int64_t)e * nchunk + ck] + rrow[k];
+                }
                 if (padded)
                     sl = r < cap_or_rows ? e * cap_or_rows + r : -1;
                 else {
@@ -557,7 +560,8 @@ hipError_t launch_dispatch_t(const LayoutPlan &p, const RowShape &rs, const uint
 #define EP_DISPATCH_CASE(N)                                                                      \
     case N:                                                                                      \
         hipLaunchKernelGGL((dispatch_kernel<N, MODE, U, LL>), grid, block, lds, s, x, H,         \
-                           topk_idx, p.K, p.E, offsets, padded, cap_or_rows, p.CT, p.nchunk,     \
+                           topk_idx, p.K, p.E, offsets, padded, cap_or_rows, p.CT, p.CE,         \
+                           p.nchunk,                                                             \
                            hist, rank, recv_x, recv_s, slot, recv_src, num_dropped, tok_amax,    \
                            recv_count, num_invalid);                                             \
         break;

@@ -12,6 +12,8 @@ namespace ep {
 struct LayoutPlan {
     int T, K, E, R;
     int CT;        // tokens per chunk
+    int CE;        // entries per chunk when a row is longer than a chunk (rows
+                   // then span chunks), else 0
     int nchunk;    // ceil(T / CT)
     int waves;     // waves per chunk block
     int epl;       // entries per lane (1..32, a power of two)

@@ -64,14 +64,19 @@ __device__ void offsets_from_totals(const int32_t *tot, int E, int32_t *offsets,
         offsets[E] = total;
 }
 
-// One block per chunk of CT tokens (n = CT*K entries <= waves*64*epl).  The
-// chunk's entries are staged in shared memory; wave w walks entries
-// [w*64*epl, (w+1)*64*epl) 64 at a time.  The kernels are short-lived and
+// One block per chunk of CT tokens (n = CT*K entries <= waves*64*epl), or,
+// when one token's row is longer than that (CE > 0), per chunk of CE
+// entries, so that a row may span chunks.  The chunk's entries are staged
+// in shared memory; wave w walks entries [w*64*epl, (w+1)*64*epl) 64 at a
+// time.  Expert ranks depend only on the row-major order of the entries, so
+// they come out the same either way; the per-token work (rank marks, rank
+// keys) reads a row's entries outside the chunk from global memory, and a
+// token's rank marks are counted by the chunk its row starts in.  The kernels are short-lived and
 // each CU runs them from a cold instruction cache, so the loops are kept
 // compact (not unrolled) and their state lives in shared memory.
 __global__ void __launch_bounds__(1024)
 layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, int R, int CT,
-                    int nbits, int epl, int key_experts, int key_div,
+                    int CE, int nbits, int epl, int key_experts, int key_div,
                     int32_t *__restrict__ chunk_hist,
                     int32_t *__restrict__ local_rank, int32_t *__restrict__ rank_part,
                     int32_t *__restrict__ inval_part, uint8_t *__restrict__ is_token_in_rank,
@@ -93,10 +98,26 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int chunk = blockIdx.x;
     const bool single = nchunk == 1;
-    const int t0 = chunk * CT;
-    const int t1 = min(T, t0 + CT);
-    const int64_t base = (int64_t)t0 * K;
-    const int n = (t1 - t0) * K;
+    // the chunk's entries [base, base + n), and the tokens whose rows start
+    // in it, [t0, t1)
+    int64_t base;
+    int n, t0, t1;
+    if (CE > 0) {
+        base = (int64_t)chunk * CE;
+        n = (int)min((int64_t)CE, (int64_t)T * K - base);
+        t0 = (int)((base + K - 1) / K);
+        t1 = (int)min((int64_t)T, (base + n + K - 1) / K);
+    } else {
+        t0 = chunk * CT;
+        t1 = min(T, t0 + CT);
+        base = (int64_t)t0 * K;
+        n = (t1 - t0) * K;
+    }
+    // entry g of topk_idx (row-major): staged when in the chunk
+    auto entry_at = [&](int64_t g) -> int {
+        const int64_t i = g - base;
+        return (i >= 0 && i < n) ? ent[i] : topk_idx[g];
+    };
 
     // ---- stage the entries: 8 loads in flight per thread
     for (int i0 = 0; i0 < n; i0 += blockDim.x * 8) {
@@ -127,14 +148,16 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
     // becomes padding (-1) otherwise; an invalid expert stays invalid (-2).
     if (key_div > 0) {
         for (int i = tid; i < n; i += blockDim.x) {
-            const int tl = i / K, k = i - tl * K;
+            const int64_t g = base + i;
+            const int64_t row0 = g / K * K;
+            const int k = (int)(g - row0);
             const int e = ent[i];
             int key = e == -1 ? -1 : -2;
             if ((unsigned)e < (unsigned)key_experts) {
                 const int r = e / key_div;
                 key = r;
                 for (int k2 = 0; k2 < k; ++k2) {
-                    const int e2 = ent[tl * K + k2];
+                    const int e2 = entry_at(row0 + k2);
                     if ((unsigned)e2 < (unsigned)key_experts && e2 / key_div == r) {
                         key = -1;
                         break;
@@ -197,10 +220,10 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
             const int tl = tb + tid;
             uint64_t m = 0;
             if (tl < ntok) {
-                const int32_t *row = ent + tl * K;
+                const int64_t row0 = (int64_t)(t0 + tl) * K;
 #pragma unroll 8
                 for (int k = 0; k < K; ++k) {
-                    const int ee = row[k];
+                    const int ee = entry_at(row0 + k);
                     if ((unsigned)ee < (unsigned)E)
                         m |= 1ull << (R == 1 ? 0 : ee / per_rank);
                 }
@@ -216,18 +239,18 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
         }
     } else {
         for (int tl = tid; tl < ntok; tl += blockDim.x) {
-            const int32_t *row = ent + tl * K;
+            const int64_t row0 = (int64_t)(t0 + tl) * K;
             if (is_token_in_rank)
                 for (int r = 0; r < R; ++r)
                     is_token_in_rank[(int64_t)(t0 + tl) * R + r] = 0;
             for (int k = 0; k < K; ++k) {
-                const int ee = row[k];
+                const int ee = entry_at(row0 + k);
                 if ((unsigned)ee >= (unsigned)E)
                     continue;
                 const int r = ee / per_rank;
                 bool first = true;
                 for (int k2 = 0; k2 < k && first; ++k2) {
-                    const int e2 = row[k2];
+                    const int e2 = entry_at(row0 + k2);
                     if ((unsigned)e2 < (unsigned)E && e2 / per_rank == r)
                         first = false;
                 }
@@ -399,22 +422,31 @@ LayoutPlan make_layout_plan(int T, int K, int E, int R)
         while (p.epl < kEpl && n > kTargetChunks * wmax_for(p.epl) * kWave * p.epl)
             p.epl *= 2;
         cap = (long long)wmax_for(p.epl) * kWave * p.epl;
-        while (cap < K && p.epl < kEpl) {   // a chunk holds at least one token
+        while (cap < K && p.epl < kEpl) {   // a chunk holds one token if it can
             p.epl *= 2;
             cap = (long long)wmax_for(p.epl) * kWave * p.epl;
         }
     }
     const int wmax = wmax_for(p.epl);
-    long long ct = cap / K;
-    if (ct < 1)
-        ct = 1;
-    if (ct > T && T > 0)
-        ct = T;
-    p.CT = (int)ct;
-    p.nchunk = T > 0 ? (int)((T + ct - 1) / ct) : 0;
     const long long per_wave = (long long)kWave * p.epl;
-    long long wv = ((long long)p.CT * K + per_wave - 1) / per_wave;
-    p.waves = wv < 1 ? 1 : (wv > wmax ? wmax : (int)wv);
+    if (cap < K) {
+        // a row longer than a chunk: chunks of cap entries, rows spanning them
+        p.CE = (int)cap;
+        p.CT = 1;
+        p.nchunk = (int)((n + cap - 1) / cap);
+        p.waves = wmax;
+    } else {
+        long long ct = cap / K;
+        if (ct < 1)
+            ct = 1;
+        if (ct > T && T > 0)
+            ct = T;
+        p.CT = (int)ct;
+        p.CE = 0;
+        p.nchunk = T > 0 ? (int)((T + ct - 1) / ct) : 0;
+        long long wv = ((long long)p.CT * K + per_wave - 1) / per_wave;
+        p.waves = wv < 1 ? 1 : (wv > wmax ? wmax : (int)wv);
+    }
     p.lds = (size_t)(p.waves * E + E + R + 32 + 2 * p.waves * per_wave) * sizeof(int32_t);
     size_t off = 256;
     p.off_hist = off;
@@ -450,13 +482,13 @@ hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *
     int32_t *rank = reinterpret_cast<int32_t *>(ws + p.off_rank);
     int32_t *rpart = reinterpret_cast<int32_t *>(ws + p.off_rpart);
     int32_t *ipart = reinterpret_cast<int32_t *>(ws + p.off_ipart);
-    if ((long long)p.CT * p.K > (long long)p.waves * kWave * p.epl)
+    if ((p.CE > 0 ? (long long)p.CE : (long long)p.CT * p.K) > (long long)p.waves * kWave * p.epl)
         return hipErrorInvalidValue;     // a chunk's entries must fit its waves
     if (p.nchunk > 0) {
         hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunk), dim3(p.waves * kWave), p.lds, s,
-                           topk_idx, p.T, p.K, p.E, p.R, p.CT, p.nbits, p.epl, p.key_experts,
-                           p.key_div, hist, rank, rpart, ipart, is_token_in_rank, counts, offsets,
-                           tokens_per_rank, num_invalid);
+                           topk_idx, p.T, p.K, p.E, p.R, p.CT, p.CE, p.nbits, p.epl,
+                           p.key_experts, p.key_div, hist, rank, rpart, ipart, is_token_in_rank,
+                           counts, offsets, tokens_per_rank, num_invalid);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess)
             return err;

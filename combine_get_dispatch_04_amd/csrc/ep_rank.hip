@@ -32,7 +32,7 @@ template <int PPT>
 __global__ void __launch_bounds__(256)
 rank_pack_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict__ topk_idx,
                  const float *__restrict__ w, int K, int E, int R, int per_rank,
-                 const int32_t *__restrict__ offsets, int max_rows, int CT, int nchunk,
+                 const int32_t *__restrict__ offsets, int max_rows, int CT, int CE, int nchunk,
                  const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ local_rank,
                  uint16_t *__restrict__ send_x, int32_t *__restrict__ send_src,
                  int32_t *__restrict__ send_idx, float *__restrict__ send_w,
@@ -81,7 +81,9 @@ rank_pack_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restric
         }
         int sl = -1;
         if (first) {
-            const int p = offsets[r] + chunk_base[(int64_t)r * nchunk + c] + rrow[k];
+            // rows longer than a layout chunk: each entry's own chunk
+            const int ck = CE > 0 ? (int)(((int64_t)t * K + k) / CE) : c;
+            const int p = offsets[r] + chunk_base[(int64_t)r * nchunk + ck] + rrow[k];
             sl = p < max_rows ? p : -1;
             if (writer) {
                 pack_pos[(int64_t)t * R + r] = sl;
@@ -274,7 +276,8 @@ hipError_t launch_rank_pack(const RankPlan &rp, const uint16_t *x, int H, const 
 #define EP_PACK_CASE(N)                                                                           \
     case N:                                                                                       \
         hipLaunchKernelGGL((rank_pack_kernel<N>), grid, block, 0, s, x, H, topk_idx, w, p.K, E, R, \
-                           E / R, rank_offsets, max_rows, p.CT, p.nchunk, hist, rank, send_x,     \
+                           E / R, rank_offsets, max_rows, p.CT, p.CE, p.nchunk, hist, rank,       \
+                           send_x,                                                                \
                            send_src, send_idx, send_w, pack_pos, num_dropped);                    \
         break;
     switch (sh.ppt) {

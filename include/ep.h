@@ -109,7 +109,8 @@ size_t ep_ec_workspace_bytes(int T, int E, int C);
  *                     ep_dispatch, which must get the same ws, topk_idx, T,
  *                     K and E on the same stream with no other use of ws in
  *                     between.
- * Constraints: T >= 0, K >= 1, 1 <= E <= 4096, 1 <= R <= 1024, E % R == 0.
+ * Constraints: T >= 0, K >= 1 (no other limit: T*K < 2^31), 1 <= E <= 4096,
+ * 1 <= R <= 1024, E % R == 0.
  */
 ep_status_t ep_get_dispatch_layout(const int32_t *topk_idx, int T, int K, int E, int R,
                                    int32_t *counts, int32_t *offsets,

@@ -48,7 +48,8 @@ int main()
     expect(ep_workspace_bytes(10, 0, 256, 1) == 0, "K = 0", 0, 0);
     expect(ep_workspace_bytes(10, 8, 4097, 1) == 0, "E beyond 4096", 4097, 0);
     expect(ep_workspace_bytes(10, 8, 256, 3) == 0, "E % R != 0", 256, 3);
-    expect(ep_workspace_bytes(10, 1025, 256, 1) == 0, "K beyond 1024", 1025, 0);
+    expect(ep_workspace_bytes(10, 1025, 256, 1) > 0, "K beyond 1024 is accepted", 1025, 0);
+    expect(ep_workspace_bytes(5, 1 << 29, 256, 1) == 0, "T*K beyond 2^31", 5, 1 << 29);
 
     const long long Cs[] = {1, 3, 256, 4096, 1 << 20};
     for (long long C : Cs)

@@ -62,6 +62,9 @@ def test_workspace_sizes():
     assert N.ep_workspace_bytes(10, 2, 6, 4) == 0           # E % R != 0
     assert N.ep_workspace_bytes(10, 2, 5000, 1) == 0        # E too large
     assert N.ep_workspace_bytes(-1, 2, 4, 1) == 0
+    assert N.ep_workspace_bytes(3, 40000, 256, 16) >= 3 * 40000 * 4   # rows longer than a chunk
+    assert N.ep_workspace_bytes(1, (1 << 31) - 1, 8, 1) > 0             # T*K just below 2^31
+    assert N.ep_workspace_bytes(2, 1 << 30, 8, 1) == 0                 # T*K = 2^31
     assert N.ep_ec_workspace_bytes(8192, 64, 256) >= 64 * 256 * 4 + 8193 * 8
     assert N.ep_ec_workspace_bytes(8, 0, 4) == 0
 

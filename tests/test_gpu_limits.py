@@ -1,9 +1,10 @@
 """GPU parity at the documented limits of the C ABI (include/ep.h):
-top-k up to 1024 ("[Feature Request] Support Expert-Choice Routing via
-Native Expert-Centric API", Current Limitation: the 32-expert cap is lifted
-here), E = 4096 experts with R = 1024 ranks, rows of 2^20 channels (many row
-segments per token), and a large token count with K = 1.  Every result is
-compared with the oracle like the other parity tests.
+top-k of 1024 and beyond ("[Feature Request] Support Expert-Choice Routing
+via Native Expert-Centric API", Current Limitation: the 32-expert cap is
+lifted here; a token's row longer than a layout chunk spans chunks), E = 4096
+experts with R = 1024 ranks, rows of 2^20 channels (many row segments per
+token), and a large token count with K = 1.  Every result is compared with
+the oracle like the other parity tests.
 """
 import sys
 
@@ -113,3 +114,59 @@ def test_many_tokens_top1():
     _announce("T=300000 K=1")
     c = W.random_token_choice(35, 300000, 8, 7, 1, p_pad=0.05, p_invalid=0.01, p_dup=0.0)
     _round_trip(c)
+
+
+# Rows longer than one layout chunk (the chunk holds 1024 entries at E = 4096
+# and about 7000 at E = 64): the layout chunks by entries and a token's row
+# spans chunks; the per-token rank marks read the row's other entries from
+# global memory.
+LONG_ROWS = [
+    # seed, T, H, E, K, R
+    (41, 7, 64, 4096, 1500, 8),
+    (42, 40, 64, 4096, 3000, 1024),      # ranks beyond 64: the per-token rank path
+    (43, 5, 32, 64, 10000, 4),
+    (44, 3, 16, 256, 40000, 16),
+    (45, 300, 32, 4096, 1100, 64),      # several tokens per chunk boundary pattern
+]
+
+
+@pytest.mark.parametrize("seed,T,H,E,K,R", LONG_ROWS)
+def test_rows_longer_than_a_layout_chunk(seed, T, H, E, K, R):
+    _announce(f"long rows T={T} E={E} K={K} R={R}")
+    c = W.random_token_choice(seed, T, H, E, K, p_pad=0.2, p_invalid=0.01, p_dup=0.2)
+    L = G.layout(G.dev(c.topk_idx), c.E, R)
+    torch.cuda.synchronize()
+    ref = oracle.layout(c.topk_idx, c.E, R)
+    for key in ("counts", "offsets", "tokens_per_rank", "is_token_in_rank"):
+        assert np.array_equal(G.host(L[key]), ref[key]), key
+    assert int(G.host(L["num_invalid"])[0]) == ref["num_invalid"]
+    _round_trip(c)
+    # the padded form and an fp8 dispatch take the same per-entry chunk bases
+    x_d, idx_d = G.dev(c.x), G.dev(c.topk_idx)
+    L1 = G.layout(idx_d, c.E)
+    cap = 2
+    recv, _, slot, _, nd = G.dispatch(x_d, idx_d, c.E, L1, True, cap)
+    torch.cuda.synchronize()
+    s_ref, _, nd_ref = oracle.slots(c.topk_idx, c.E, True, cap)
+    assert np.array_equal(G.host(slot), s_ref)
+    assert int(G.host(nd)[0]) == nd_ref
+    if H % 128 == 0:
+        _round_trip(c, N.EP_QUANT_FP8_E4M3_G128)
+
+
+@pytest.mark.parametrize("seed,T,H,E,K,R", [(46, 9, 64, 4096, 2500, 64), (47, 4, 32, 4096, 4000, 1024),
+                                            (48, 6, 16, 64, 9000, 8)])
+def test_rank_pack_with_rows_longer_than_a_chunk(seed, T, H, E, K, R):
+    """The sender pack's rank keys and first-on-rank tests across chunks."""
+    _announce(f"long rows pack T={T} E={E} K={K} R={R}")
+    c = W.random_token_choice(seed, T, H, E, K, p_pad=0.2, p_invalid=0.01, p_dup=0.2)
+    o = G.pack_by_rank(G.dev(c.x), G.dev(c.topk_idx), G.dev(c.topk_weights), E, R)
+    torch.cuda.synchronize()
+    ref = oracle.rank_pack(c.x, c.topk_idx, c.topk_weights, E, R)
+    n = int(ref["rank_offsets"][R])
+    assert np.array_equal(G.host(o["rank_offsets"]), ref["rank_offsets"])
+    assert np.array_equal(G.host(o["pack_pos"]), ref["pack_pos"])
+    assert np.array_equal(G.host(o["send_src"][:n]), ref["send_src"][:n])
+    assert np.array_equal(G.host(o["send_idx"][:n]), ref["send_idx"][:n])
+    assert np.array_equal(G.host(o["send_w"][:n]).view(np.uint32), ref["send_w"][:n].view(np.uint32))
+    assert np.array_equal(G.host(o["send_x"][:n]), ref["send_x"][:n])
