@@ -12,7 +12,13 @@
 //   token's entries in ascending order, received rows equal their tokens'
 //   rows, and the unit-weight combine gives bf16(picks_t * x_t);
 //   the one-launch low-latency dispatch: expert e's rows in ascending (t,k)
-//   from e*cap, capacity overflow dropped and counted, recv_count.
+//   from e*cap, capacity overflow dropped and counted, recv_count;
+//   one rank's share of the exchange (API Overview: get_dispatch_layout's
+//   num_tokens_per_rank / is_token_in_rank, dispatch to the experts' ranks,
+//   combine): the pack's rows grouped by rank in token order with the local
+//   ids, the receiver's scatter, partial sums, and the sum over ranks giving
+//   bf16(m_t * x_t) exactly with unit weights;
+//   the no-allocation layout + dispatch: the same slots and rows as the pair.
 // Exit status 0 = every check passed.  Built by tests/capi/build.py.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -314,6 +320,189 @@ static int low_latency()
     return 0;
 }
 
+static int rank_share()
+{
+    const int T = 2000, H = 512, E = 64, K = 6, R = 8, per = E / R;
+    const int64_t TK = (int64_t)T * K;
+    std::vector<int32_t> idx(TK);
+    for (auto &v : idx) {
+        const uint32_t u = rnd() % 100;
+        v = u < 15 ? -1 : (int32_t)(rnd() % E);
+    }
+    std::vector<uint16_t> x((size_t)T * H);
+    for (auto &v : x)
+        v = (uint16_t)(((rnd() & 1u) << 15) | ((uint32_t)(110 + rnd() % 30) << 7) | (rnd() & 0x7Fu));
+    const int max_rows = T * (K < R ? K : R);
+    int32_t *d_idx, *d_tpr, *d_roff, *d_src, *d_sidx, *d_pos, *d_nd;
+    float *d_sw, *d_part;
+    uint16_t *d_x, *d_sx, *d_out;
+    void *d_ws;
+    const size_t wsb = ep_pack_workspace_bytes(T, K, E, R);
+    HIP_OK(hipMalloc(&d_idx, TK * 4));
+    HIP_OK(hipMalloc(&d_tpr, R * 4));
+    HIP_OK(hipMalloc(&d_roff, (R + 1) * 4));
+    HIP_OK(hipMalloc(&d_src, (size_t)max_rows * 4));
+    HIP_OK(hipMalloc(&d_sidx, (size_t)max_rows * K * 4));
+    HIP_OK(hipMalloc(&d_sw, (size_t)max_rows * K * 4));
+    HIP_OK(hipMalloc(&d_pos, (size_t)T * R * 4));
+    HIP_OK(hipMalloc(&d_nd, 4));
+    HIP_OK(hipMalloc(&d_x, (size_t)T * H * 2));
+    HIP_OK(hipMalloc(&d_sx, (size_t)max_rows * H * 2));
+    HIP_OK(hipMalloc(&d_out, (size_t)T * H * 2));
+    HIP_OK(hipMalloc(&d_ws, wsb));
+    HIP_OK(hipMemcpy(d_idx, idx.data(), TK * 4, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(d_x, x.data(), (size_t)T * H * 2, hipMemcpyHostToDevice));
+    EP_OK_(ep_pack_by_rank(d_x, T, H, d_idx, nullptr, K, E, R, max_rows, d_tpr, d_roff, d_sx,
+                           d_src, d_sidx, d_sw, d_pos, d_nd, d_ws, wsb, nullptr));
+    HIP_OK(hipDeviceSynchronize());
+    std::vector<int32_t> roff(R + 1), tpr(R), pos((size_t)T * R);
+    int32_t nd;
+    HIP_OK(hipMemcpy(roff.data(), d_roff, (R + 1) * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(tpr.data(), d_tpr, R * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(pos.data(), d_pos, (size_t)T * R * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(&nd, d_nd, 4, hipMemcpyDeviceToHost));
+    const int S = roff[R];
+    std::vector<int32_t> src(S), sidx((size_t)S * K);
+    std::vector<float> sw((size_t)S * K);
+    std::vector<uint16_t> sx((size_t)S * H);
+    HIP_OK(hipMemcpy(src.data(), d_src, (size_t)S * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(sidx.data(), d_sidx, (size_t)S * K * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(sw.data(), d_sw, (size_t)S * K * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(sx.data(), d_sx, (size_t)S * H * 2, hipMemcpyDeviceToHost));
+    expect(nd == 0 && roff[0] == 0, "pack: no drop, rank 0 starts at row 0", nd);
+    int local_entries = 0;
+    for (int r = 0; r < R; ++r) {
+        expect(roff[r + 1] - roff[r] == tpr[r], "pack: offsets are the prefix of tokens_per_rank", r);
+        int expect_rows = 0, last_t = -1;
+        for (int t = 0; t < T; ++t) {
+            bool on = false;
+            for (int k = 0; k < K; ++k)
+                on = on || (idx[(int64_t)t * K + k] >= 0 && idx[(int64_t)t * K + k] / per == r);
+            const int p = pos[(size_t)t * R + r];
+            expect(on == (p >= 0), "pack: a row exactly for the ranks the token uses", t);
+            if (!on)
+                continue;
+            ++expect_rows;
+            expect(p >= roff[r] && p < roff[r + 1] && src[p] == t, "pack: row in its rank's block", p);
+            if (p < 0 || p >= S)
+                continue;
+            expect(t > last_t, "pack: ascending tokens inside a rank", t);
+            last_t = t;
+            expect(memcmp(&sx[(size_t)p * H], &x[(size_t)t * H], (size_t)H * 2) == 0,
+                   "pack: the row is the token's row", p);
+            for (int k = 0; k < K; ++k) {
+                const int e = idx[(int64_t)t * K + k];
+                const bool here = e >= 0 && e / per == r;
+                expect(sidx[(size_t)p * K + k] == (here ? e - r * per : -1), "pack: local ids", p);
+                expect(sw[(size_t)p * K + k] == (here ? 1.0f : 0.0f), "pack: unit weights", p);
+                local_entries += here;
+            }
+        }
+        expect(expect_rows == tpr[r], "pack: tokens_per_rank", r);
+    }
+    // the receiver: its blocks concatenated, scattered into E/R experts
+    int32_t *d_counts, *d_off, *d_ninv, *d_slot, *d_rsrc, *d_rnd;
+    uint16_t *d_recv;
+    void *d_rws;
+    const size_t rwsb = ep_workspace_bytes(S, K, per, 1);
+    HIP_OK(hipMalloc(&d_counts, per * 4));
+    HIP_OK(hipMalloc(&d_off, (per + 1) * 4));
+    HIP_OK(hipMalloc(&d_ninv, 4));
+    HIP_OK(hipMalloc(&d_slot, (size_t)S * K * 4));
+    HIP_OK(hipMalloc(&d_rsrc, (size_t)local_entries * 4));
+    HIP_OK(hipMalloc(&d_rnd, 4));
+    HIP_OK(hipMalloc(&d_recv, (size_t)local_entries * H * 2));
+    HIP_OK(hipMalloc(&d_part, (size_t)S * H * 4));
+    HIP_OK(hipMalloc(&d_rws, rwsb));
+    EP_OK_(ep_get_dispatch_layout(d_sidx, S, K, per, 1, d_counts, d_off, nullptr, nullptr, d_ninv,
+                                  d_rws, rwsb, nullptr));
+    EP_OK_(ep_dispatch(d_sx, S, H, d_sidx, K, per, d_off, EP_LAYOUT_CONTIGUOUS, local_entries,
+                       EP_QUANT_BF16, d_recv, nullptr, d_slot, d_rsrc, d_rnd, d_rws, rwsb, nullptr));
+    EP_OK_(ep_combine_partial(d_recv, local_entries, H, d_slot, d_sw, S, K, d_part, nullptr));
+    EP_OK_(ep_combine_ranks(d_part, S, H, d_pos, T, R, d_out, nullptr));
+    HIP_OK(hipDeviceSynchronize());
+    std::vector<uint16_t> out((size_t)T * H);
+    int32_t rnd_;
+    HIP_OK(hipMemcpy(out.data(), d_out, (size_t)T * H * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(&rnd_, d_rnd, 4, hipMemcpyDeviceToHost));
+    expect(rnd_ == 0, "receiver: nothing dropped", rnd_);
+    for (int t = 0; t < T; ++t) {
+        int m = 0;
+        for (int k = 0; k < K; ++k)
+            m += idx[(int64_t)t * K + k] >= 0;
+        for (int h = 0; h < H; ++h) {
+            const float pv = (float)m * bf16_value(x[(size_t)t * H + h]);
+            expect(out[(size_t)t * H + h] == bf16_nearest(pv), "sum over ranks = bf16(m_t x_t)", t);
+        }
+    }
+    hipFree(d_idx); hipFree(d_tpr); hipFree(d_roff); hipFree(d_src); hipFree(d_sidx);
+    hipFree(d_sw); hipFree(d_pos); hipFree(d_nd); hipFree(d_x); hipFree(d_sx); hipFree(d_out);
+    hipFree(d_ws); hipFree(d_counts); hipFree(d_off); hipFree(d_ninv); hipFree(d_slot);
+    hipFree(d_rsrc); hipFree(d_rnd); hipFree(d_recv); hipFree(d_part); hipFree(d_rws);
+    return 0;
+}
+
+// The no-allocation call against the pair on the same input (with a
+// caller workspace): identical counts, offsets, slots and rows.
+static int no_alloc()
+{
+    const int T = 1500, H = 256, E = 32, K = 4;
+    const int64_t TK = (int64_t)T * K;
+    std::vector<int32_t> idx(TK);
+    for (auto &v : idx)
+        v = rnd() % 10 == 0 ? -1 : (int32_t)(rnd() % E);
+    std::vector<uint16_t> x((size_t)T * H);
+    for (auto &v : x)
+        v = (uint16_t)rnd();
+    for (auto &v : x)
+        v &= 0xBFFF;                      // finite values
+    const int rows = (int)TK;
+    int32_t *d_idx, *b[2][5];
+    uint16_t *d_x, *d_recv[2];
+    void *d_ws;
+    const size_t wsb = ep_workspace_bytes(T, K, E, 1);
+    HIP_OK(hipMalloc(&d_idx, TK * 4));
+    HIP_OK(hipMalloc(&d_x, (size_t)T * H * 2));
+    HIP_OK(hipMalloc(&d_ws, wsb));
+    for (int i = 0; i < 2; ++i) {
+        HIP_OK(hipMalloc(&b[i][0], E * 4));            // counts
+        HIP_OK(hipMalloc(&b[i][1], (E + 1) * 4));      // offsets
+        HIP_OK(hipMalloc(&b[i][2], 4));                // num_invalid
+        HIP_OK(hipMalloc(&b[i][3], TK * 4));           // slot
+        HIP_OK(hipMalloc(&b[i][4], 4));                // num_dropped
+        HIP_OK(hipMalloc(&d_recv[i], (size_t)rows * H * 2));
+        HIP_OK(hipMemset(d_recv[i], 0, (size_t)rows * H * 2));
+    }
+    HIP_OK(hipMemcpy(d_idx, idx.data(), TK * 4, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(d_x, x.data(), (size_t)T * H * 2, hipMemcpyHostToDevice));
+    EP_OK_(ep_get_dispatch_layout(d_idx, T, K, E, 1, b[0][0], b[0][1], nullptr, nullptr, b[0][2],
+                                  d_ws, wsb, nullptr));
+    EP_OK_(ep_dispatch(d_x, T, H, d_idx, K, E, b[0][1], EP_LAYOUT_CONTIGUOUS, rows, EP_QUANT_BF16,
+                       d_recv[0], nullptr, b[0][3], nullptr, b[0][4], d_ws, wsb, nullptr));
+    EP_OK_(ep_layout_dispatch_noalloc(d_x, T, H, d_idx, K, E, 1, b[1][0], b[1][1], nullptr,
+                                      nullptr, b[1][2], EP_LAYOUT_CONTIGUOUS, rows, EP_QUANT_BF16,
+                                      d_recv[1], nullptr, b[1][3], nullptr, b[1][4], nullptr));
+    HIP_OK(hipDeviceSynchronize());
+    const size_t n[5] = {(size_t)E, (size_t)E + 1, 1, (size_t)TK, 1};
+    for (int j = 0; j < 5; ++j) {
+        std::vector<int32_t> a(n[j]), c(n[j]);
+        HIP_OK(hipMemcpy(a.data(), b[0][j], n[j] * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(c.data(), b[1][j], n[j] * 4, hipMemcpyDeviceToHost));
+        expect(a == c, "no-alloc: the pair's counts, offsets, counters and slots", j);
+    }
+    std::vector<uint16_t> r0((size_t)rows * H), r1((size_t)rows * H);
+    HIP_OK(hipMemcpy(r0.data(), d_recv[0], r0.size() * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(r1.data(), d_recv[1], r1.size() * 2, hipMemcpyDeviceToHost));
+    expect(r0 == r1, "no-alloc: the pair's receive rows", 0);
+    for (int i = 0; i < 2; ++i) {
+        for (int j = 0; j < 5; ++j)
+            hipFree(b[i][j]);
+        hipFree(d_recv[i]);
+    }
+    hipFree(d_idx); hipFree(d_x); hipFree(d_ws);
+    return 0;
+}
+
 int main()
 {
     int dev_count = 0;
@@ -322,7 +511,7 @@ int main()
         fprintf(stderr, "no GPU\n");
         return 2;
     }
-    if (token_choice() || low_latency() || expert_choice())
+    if (token_choice() || low_latency() || expert_choice() || rank_share() || no_alloc())
         return 2;
     if (failures) {
         fprintf(stderr, "%d check(s) failed\n", failures);

@@ -1,9 +1,11 @@
 """The C ABI from a plain C++ host program (tests/capi/roundtrip.cpp):
-hipMalloc'd buffers, the five entry points on the null stream, results
-checked on the host by properties that hold at any size (counts and
-offsets, the slot bijection and its order, received rows equal to their
-source rows, and the exact unit-weight round trip bf16(m_t * x_t)), for
-token choice and expert choice.  No Python between the caller and libep."""
+hipMalloc'd buffers, the entry points on the null stream, results checked
+on the host by properties that hold at any size (counts and offsets, the
+slot bijection and its order, received rows equal to their source rows, and
+the exact unit-weight round trip bf16(m_t * x_t)), for token choice, the
+one-launch low-latency dispatch, expert choice and one rank's share of the
+exchange; and the no-allocation call equal to the pair.  No Python between
+the caller and libep."""
 import os
 import subprocess
 
