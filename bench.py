@@ -73,6 +73,7 @@ KERNEL_SOURCES = {
     "layout_scan_kernel": ["ep_layout.hip"],
     "dispatch_kernel": ["ep_dispatch.hip", "ep_layout.hip"],
     "combine_kernel": ["ep_combine.hip"],
+    "partial_kernel": ["ep_combine.hip"],
     "ec_dispatch_fused_kernel": ["ep_expert_choice.hip"],
     "ec_combine_kernel": ["ep_combine.hip"],
     "rank_pack_kernel": ["ep_rank.hip", "ep_layout.hip"],
@@ -454,7 +455,7 @@ def ranks_path(c, N, torch, dev, sp, R):
            "partial": n_valid * H * 2 + S * H * 4 + meta_b,
            "rank_sum": S * H * 4 + T * H * 2 + T * R * 4}
     kern = {"pack": "rank_pack_kernel", "layout": "layout_chunk_kernel",
-            "dispatch": "dispatch_kernel", "partial": "combine_kernel",
+            "dispatch": "dispatch_kernel", "partial": "partial_kernel",
             "rank_sum": "rank_sum_kernel"}
     meta = {"T": T, "H": H, "E": E, "top_k": K, "ranks": R, "experts_per_rank": per,
             "quant": "bf16", "recv_layout": "contiguous", "combine": "weighted",

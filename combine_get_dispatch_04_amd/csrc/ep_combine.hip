@@ -16,9 +16,9 @@
 // order, then rounds once to bf16 (nearest even).  A token with no source
 // row writes +0.
 //
-// The receiving rank of the expert-parallel exchange uses the token-choice
-// kernel with fp32 output rows (F32): its partial sums per received row
-// travel back to the sender, which adds them over ranks (ep_rank.hip).
+// The receiving rank of the expert-parallel exchange sums the same way into
+// fp32 rows (partial_kernel): its partial sums per received row travel back
+// to the sender, which adds them over ranks (ep_rank.hip).
 #include "ep_common.h"
 #include "ep_internal.h"
 
@@ -48,43 +48,34 @@ __device__ __forceinline__ void acc_row(float (&acc)[PPT][8], const char *src, f
     }
 }
 
-// bf16 rows (16 bytes per 8 channels), or fp32 rows (32 bytes) when F32.
-template <int PPT, bool F32 = false>
-__device__ __forceinline__ void store_row(const float (&acc)[PPT][8], void *out, int H, int t,
+// bf16 rows: 16 bytes per 8 channels.
+template <int PPT>
+__device__ __forceinline__ void store_row(const float (&acc)[PPT][8], uint16_t *out, int H, int t,
                                           int seg0, int pieces)
 {
-    char *dst = reinterpret_cast<char *>(out) + (size_t)t * H * (F32 ? 4 : 2);
+    char *dst = reinterpret_cast<char *>(out) + (size_t)t * H * 2;
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
         int i = seg0 + threadIdx.x + j * blockDim.x;
         if (i < pieces) {
-            if constexpr (F32) {
-                st16(dst + (size_t)i * 32, u32x4{__float_as_uint(acc[j][0]), __float_as_uint(acc[j][1]),
-                                                 __float_as_uint(acc[j][2]), __float_as_uint(acc[j][3])});
-                st16(dst + (size_t)i * 32 + 16,
-                     u32x4{__float_as_uint(acc[j][4]), __float_as_uint(acc[j][5]),
-                           __float_as_uint(acc[j][6]), __float_as_uint(acc[j][7])});
-            } else {
-                u32x4 o;
-                o.x = pack_bf16x2(acc[j][0], acc[j][1]);
-                o.y = pack_bf16x2(acc[j][2], acc[j][3]);
-                o.z = pack_bf16x2(acc[j][4], acc[j][5]);
-                o.w = pack_bf16x2(acc[j][6], acc[j][7]);
-                st16(dst + (size_t)i * 16, o);
-            }
+            u32x4 o;
+            o.x = pack_bf16x2(acc[j][0], acc[j][1]);
+            o.y = pack_bf16x2(acc[j][2], acc[j][3]);
+            o.z = pack_bf16x2(acc[j][4], acc[j][5]);
+            o.w = pack_bf16x2(acc[j][6], acc[j][7]);
+            st16(dst + (size_t)i * 16, o);
         }
     }
 }
 
 // G == 1: one source row per round, its slot and weight scalar loads; slots
 // outside [0, y_rows) are skipped.  G > 1: G valid source rows per round,
-// all G*PPT row pieces requested before the first FMA.  F32: fp32 output
-// rows (the partial sums of the exchange) instead of bf16.
-template <int PPT, int G, bool F32 = false>
+// all G*PPT row pieces requested before the first FMA.
+template <int PPT, int G>
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint16_t *__restrict__ y, int y_rows, int H,
                const int32_t *__restrict__ slot, const float *__restrict__ w, int K,
-               void *__restrict__ out)
+               uint16_t *__restrict__ out)
 {
     const int t = blockIdx.x;
     const int pieces = H >> 3;
@@ -162,7 +153,84 @@ combine_kernel(const uint16_t *__restrict__ y, int y_rows, int H,
             }
         }
     }
-    store_row<PPT, F32>(acc, out, H, t, seg0, pieces);
+    store_row<PPT>(acc, out, H, t, seg0, pieces);
+}
+
+// The receiving rank's partial sums: fp32 output rows.  A unit is 4
+// channels (8 bytes of y, 16 bytes of output), so that each store
+// instruction of a wave writes 1 KiB of a row with no gaps.  Each round takes
+// the row's next G valid slots in ascending k (one load of 64 slots per wave,
+// a ballot, readlane), requests all of their pieces, then adds them in order
+// with fp32 FMAs.
+template <int PPT, int G>
+__global__ void __launch_bounds__(256)
+partial_kernel(const uint16_t *__restrict__ y, int y_rows, int H,
+               const int32_t *__restrict__ slot, const float *__restrict__ w, int K,
+               float *__restrict__ out)
+{
+    const int t = blockIdx.x;
+    const int units = H >> 2;
+    const int seg0 = blockIdx.y * PPT * blockDim.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    float acc[PPT][4];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            acc[j][u] = 0.0f;
+    const int32_t *srow = slot + (int64_t)t * K;
+    const float *wrow = w ? w + (int64_t)t * K : nullptr;
+    for (int k0 = 0; k0 < K; k0 += kWave) {
+        const int kk = k0 + lane;
+        const int sv = kk < K ? srow[kk] : -1;
+        const bool valid = (unsigned)sv < (unsigned)y_rows;
+        const float wv = valid ? (wrow ? wrow[kk] : 1.0f) : 0.0f;
+        uint64_t m = ballot(valid);
+        while (m) {
+            int sel[G];
+            float wk[G];
+            bool ok[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                ok[g] = m != 0;
+                const int b = ok[g] ? (int)__builtin_ctzll(m) : 0;
+                m &= m - 1;
+                sel[g] = ok[g] ? __builtin_amdgcn_readlane(sv, b) : 0;
+                wk[g] = ok[g] ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), b))
+                              : 0.0f;
+            }
+            u32x2 v[G][PPT];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const rsrc_t src = row_rsrc(reinterpret_cast<const char *>(y) +
+                                                (size_t)sel[g] * H * 2,
+                                            ok[g] ? units * 8 : 0);
+#pragma unroll
+                for (int j = 0; j < PPT; ++j)
+                    v[g][j] = row_ld8(src, (seg0 + threadIdx.x + j * blockDim.x) * 8);
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (!ok[g])
+                    continue;
+#pragma unroll
+                for (int j = 0; j < PPT; ++j) {
+                    acc[j][0] = fmaf(wk[g], bf16_lo(v[g][j].x), acc[j][0]);
+                    acc[j][1] = fmaf(wk[g], bf16_hi(v[g][j].x), acc[j][1]);
+                    acc[j][2] = fmaf(wk[g], bf16_lo(v[g][j].y), acc[j][2]);
+                    acc[j][3] = fmaf(wk[g], bf16_hi(v[g][j].y), acc[j][3]);
+                }
+            }
+        }
+    }
+    float *dst = out + (size_t)t * H;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int i = seg0 + threadIdx.x + j * blockDim.x;
+        if (i < units)
+            st16(dst + (size_t)i * 4, u32x4{__float_as_uint(acc[j][0]), __float_as_uint(acc[j][1]),
+                                            __float_as_uint(acc[j][2]), __float_as_uint(acc[j][3])});
+    }
 }
 
 // G entries per round: their row indices and weights are scalar loads, then
@@ -266,9 +334,8 @@ RowShape row_shape(int pieces, int maxppt)
         return hipErrorInvalidValue; \
     }
 
-template <bool F32>
-hipError_t launch_combine_t(const uint16_t *y, int y_rows, int H, const int32_t *slot,
-                            const float *w, int T, int K, void *out, hipStream_t s)
+hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot,
+                          const float *w, int T, int K, uint16_t *out, hipStream_t s)
 {
     if (T == 0)
         return hipSuccess;
@@ -288,21 +355,21 @@ hipError_t launch_combine_t(const uint16_t *y, int y_rows, int H, const int32_t 
         return hipErrorInvalidConfiguration;
     dim3 grid(T, rs.nseg), block(rs.bd);
     if (few) {
-        hipLaunchKernelGGL((combine_kernel<1, 8, F32>), grid, block, 0, s, y, y_rows, H, slot, w,
+        hipLaunchKernelGGL((combine_kernel<1, 8>), grid, block, 0, s, y, y_rows, H, slot, w,
                            K, out);
         return hipGetLastError();
     }
 #define EP_COMBINE_CASE(N)                                                                       \
     case N:                                                                                      \
-        hipLaunchKernelGGL((combine_kernel<N, 1, F32>), grid, block, 0, s, y, y_rows, H, slot, w, \
+        hipLaunchKernelGGL((combine_kernel<N, 1>), grid, block, 0, s, y, y_rows, H, slot, w, \
                            K, out);                                                              \
         break;
     if (many) {
         if (rs.ppt == 1)
-            hipLaunchKernelGGL((combine_kernel<1, 4, F32>), grid, block, 0, s, y, y_rows, H, slot,
+            hipLaunchKernelGGL((combine_kernel<1, 4>), grid, block, 0, s, y, y_rows, H, slot,
                                w, K, out);
         else
-            hipLaunchKernelGGL((combine_kernel<2, 4, F32>), grid, block, 0, s, y, y_rows, H, slot,
+            hipLaunchKernelGGL((combine_kernel<2, 4>), grid, block, 0, s, y, y_rows, H, slot,
                                w, K, out);
         return hipGetLastError();
     }
@@ -311,16 +378,67 @@ hipError_t launch_combine_t(const uint16_t *y, int y_rows, int H, const int32_t 
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const uint16_t *y, int y_rows, int H, const int32_t *slot,
-                          const float *w, int T, int K, uint16_t *out, hipStream_t s)
-{
-    return launch_combine_t<false>(y, y_rows, H, slot, w, T, K, out, s);
-}
-
 hipError_t launch_combine_partial(const uint16_t *y, int y_rows, int H, const int32_t *slot,
                                   const float *w, int S, int K, float *partial, hipStream_t s)
 {
-    return launch_combine_t<true>(y, y_rows, H, slot, w, S, K, partial, s);
+    if (S == 0)
+        return hipSuccess;
+    // The shapes of the bf16 combine in units of 4 channels (the same bytes
+    // per thread): few rows with K < 12 take 8 slots per round, many source
+    // slots (K >= 12) or few rows 4, otherwise 2 (a received row has few
+    // valid slots: at prefill with 8 ranks, 1.4 on average).
+    const bool many = K >= 12 || S < 1024;
+    const bool few = S < 1024 && K < 12;
+    RowShape rs = row_shape(H / 4, few ? 2 : (many ? 4 : 16));
+    if ((uint64_t)S * rs.bd > 0xFFFFFFFFull)
+        return hipErrorInvalidConfiguration;
+    dim3 grid(S, rs.nseg), block(rs.bd);
+#define EP_PARTIAL_LAUNCH(N, G_)                                                                \
+    hipLaunchKernelGGL((partial_kernel<N, G_>), grid, block, 0, s, y, y_rows, H, slot, w, K,    \
+                       partial)
+    if (few) {
+        if (rs.ppt == 1)
+            EP_PARTIAL_LAUNCH(1, 8);
+        else
+            EP_PARTIAL_LAUNCH(2, 8);
+        return hipGetLastError();
+    }
+    if (many) {
+        switch (rs.ppt) {
+        case 1: EP_PARTIAL_LAUNCH(1, 4); break;
+        case 2: EP_PARTIAL_LAUNCH(2, 4); break;
+        case 3: EP_PARTIAL_LAUNCH(3, 4); break;
+        default: EP_PARTIAL_LAUNCH(4, 4); break;
+        }
+        return hipGetLastError();
+    }
+#define EP_PARTIAL_CASE(N) \
+    case N:                \
+        EP_PARTIAL_LAUNCH(N, 2); \
+        break;
+    switch (rs.ppt) {
+        EP_PARTIAL_CASE(1)
+        EP_PARTIAL_CASE(2)
+        EP_PARTIAL_CASE(3)
+        EP_PARTIAL_CASE(4)
+        EP_PARTIAL_CASE(5)
+        EP_PARTIAL_CASE(6)
+        EP_PARTIAL_CASE(7)
+        EP_PARTIAL_CASE(8)
+        EP_PARTIAL_CASE(9)
+        EP_PARTIAL_CASE(10)
+        EP_PARTIAL_CASE(11)
+        EP_PARTIAL_CASE(12)
+        EP_PARTIAL_CASE(13)
+        EP_PARTIAL_CASE(14)
+        EP_PARTIAL_CASE(15)
+        EP_PARTIAL_CASE(16)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef EP_PARTIAL_CASE
+#undef EP_PARTIAL_LAUNCH
+    return hipGetLastError();
 }
 
 hipError_t launch_ec_combine(const uint16_t *y, const float *w, int E, int C, int H,

@@ -62,6 +62,10 @@ __device__ __forceinline__ u32x4 row_ld16(rsrc_t r, int off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy);
 }
+__device__ __forceinline__ u32x2 row_ld8(rsrc_t r, int off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadPolicy);
+}
 // Default policy, for rows that other blocks read again.
 __device__ __forceinline__ u32x4 row_ld16_cached(rsrc_t r, int off)
 {

@@ -142,27 +142,29 @@ __global__ void rank_pack_empty_kernel(const int32_t *__restrict__ offsets, int 
     }
 }
 
-// One block per (token, row segment); a thread owns PPT units of 8 channels
-// (32 bytes of fp32 partials, 16 bytes of output).  Each round takes the
-// token's next G valid rows in rank order (one load of 64 positions per wave,
-// a ballot, readlane), requests all of their pieces, then adds them in order.
+// One block per (token, row segment); a thread owns PPT units of 4 channels
+// (16 bytes of fp32 partials, 8 bytes of output), so that each load
+// instruction of a wave reads 1 KiB of a row with no gaps.  Each round takes
+// the token's next G valid rows in rank order (one load of 64 positions per
+// wave, a ballot, readlane), requests all of their pieces, then adds them in
+// order.
 template <int PPT, int G>
 __global__ void __launch_bounds__(256)
 rank_sum_kernel(const float *__restrict__ partial, int rows, int H,
                 const int32_t *__restrict__ pack_pos, int R, uint16_t *__restrict__ out)
 {
     const int t = blockIdx.x;
-    const int units = H >> 3;
+    const int units = H >> 2;
     const int seg0 = blockIdx.y * PPT * blockDim.x;
     const int lane = threadIdx.x & (kWave - 1);
-    float acc[PPT][8];
+    float acc[PPT][4];
 #pragma unroll
     for (int j = 0; j < PPT; ++j)
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 4; ++u)
             acc[j][u] = 0.0f;
     const int32_t *prow = pack_pos + (int64_t)t * R;
-    const int rbytes = units * 32;
+    const int rbytes = units * 16;
     for (int r0 = 0; r0 < R; r0 += kWave) {
         const int rr = r0 + lane;
         const int pv = rr < R ? prow[rr] : -1;
@@ -177,18 +179,15 @@ rank_sum_kernel(const float *__restrict__ partial, int rows, int H,
                 m &= m - 1;
                 sel[g] = ok[g] ? __builtin_amdgcn_readlane(pv, b) : 0;
             }
-            u32x4 lo[G][PPT], hi[G][PPT];
+            u32x4 v[G][PPT];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const rsrc_t src = row_rsrc(reinterpret_cast<const char *>(partial) +
                                                 (size_t)sel[g] * rbytes,
                                             ok[g] ? rbytes : 0);
 #pragma unroll
-                for (int j = 0; j < PPT; ++j) {
-                    const int off = (seg0 + threadIdx.x + j * blockDim.x) * 32;
-                    lo[g][j] = row_ld16(src, off);
-                    hi[g][j] = row_ld16(src, off + 16);
-                }
+                for (int j = 0; j < PPT; ++j)
+                    v[g][j] = row_ld16(src, (seg0 + threadIdx.x + j * blockDim.x) * 16);
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -196,14 +195,10 @@ rank_sum_kernel(const float *__restrict__ partial, int rows, int H,
                     continue;
 #pragma unroll
                 for (int j = 0; j < PPT; ++j) {
-                    acc[j][0] += __uint_as_float(lo[g][j].x);
-                    acc[j][1] += __uint_as_float(lo[g][j].y);
-                    acc[j][2] += __uint_as_float(lo[g][j].z);
-                    acc[j][3] += __uint_as_float(lo[g][j].w);
-                    acc[j][4] += __uint_as_float(hi[g][j].x);
-                    acc[j][5] += __uint_as_float(hi[g][j].y);
-                    acc[j][6] += __uint_as_float(hi[g][j].z);
-                    acc[j][7] += __uint_as_float(hi[g][j].w);
+                    acc[j][0] += __uint_as_float(v[g][j].x);
+                    acc[j][1] += __uint_as_float(v[g][j].y);
+                    acc[j][2] += __uint_as_float(v[g][j].z);
+                    acc[j][3] += __uint_as_float(v[g][j].w);
                 }
             }
         }
@@ -212,14 +207,9 @@ rank_sum_kernel(const float *__restrict__ partial, int rows, int H,
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
         const int i = seg0 + threadIdx.x + j * blockDim.x;
-        if (i < units) {
-            u32x4 o;
-            o.x = pack_bf16x2(acc[j][0], acc[j][1]);
-            o.y = pack_bf16x2(acc[j][2], acc[j][3]);
-            o.z = pack_bf16x2(acc[j][4], acc[j][5]);
-            o.w = pack_bf16x2(acc[j][6], acc[j][7]);
-            st16(dst + (size_t)i * 16, o);
-        }
+        if (i < units)
+            *reinterpret_cast<u32x2 *>(dst + (size_t)i * 8) =
+                u32x2{pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3])};
     }
 }
 
@@ -301,20 +291,29 @@ hipError_t launch_rank_sum(const float *partial, int rows, int H, const int32_t 
 {
     if (T == 0)
         return hipSuccess;
-    // fp32 rows: at most 2 units (64 bytes of partials) per thread, and 8
-    // rows requested per round.  Measured at prefill, R = 8 (events, two runs
-    // each): 8 rows per round 141.9-142.0 us against 145.8 for 4 and 2; one
-    // unit per thread 146-147; 7 units per thread, one row per round, 226.
-    const Shape sh = shape_for(H / 8, 2);
+    // Units of 4 channels, at most 4 per thread, 8 rows requested per round.
+    const Shape sh = shape_for(H / 4, 4);
     if ((uint64_t)T * sh.bd > 0xFFFFFFFFull)
         return hipErrorInvalidConfiguration;
     dim3 grid(T, sh.nseg), block(sh.bd);
-    if (sh.ppt == 1)
+    switch (sh.ppt) {
+    case 1:
         hipLaunchKernelGGL((rank_sum_kernel<1, 8>), grid, block, 0, s, partial, rows, H, pack_pos,
                            R, out);
-    else
+        break;
+    case 2:
         hipLaunchKernelGGL((rank_sum_kernel<2, 8>), grid, block, 0, s, partial, rows, H, pack_pos,
                            R, out);
+        break;
+    case 3:
+        hipLaunchKernelGGL((rank_sum_kernel<3, 8>), grid, block, 0, s, partial, rows, H, pack_pos,
+                           R, out);
+        break;
+    default:
+        hipLaunchKernelGGL((rank_sum_kernel<4, 8>), grid, block, 0, s, partial, rows, H, pack_pos,
+                           R, out);
+        break;
+    }
     return hipGetLastError();
 }
 
