@@ -301,13 +301,13 @@ __device__ __forceinline__ void store_unit(rsrc_t dst, int i, int units, int H, 
 // even number of pieces, so that a lane stores 16 bytes of codes).
 //
 // LL (the one-launch low-latency form, padded rows, K <= 64): there is no
-// layout call.  Each block stages topk_idx up to its own token in shared
-// memory (dynamic: T*K entries, 64 rank counters, and E histogram bins for
-// the count block) and ranks its token's entries itself: the rank of (t,k) is the
-// number of entries before it in row-major order with the same expert, the
-// same stable counting sort the layout performs.  One more block (grid.x =
-// T + 1) writes the per-expert received counts, the dropped and the invalid
-// counts.
+// layout call.  Each block reads topk_idx up to its own token and ranks its
+// token's entries itself: the rank of (t,k) is the number of entries before
+// it in row-major order with the same expert, the same stable counting sort
+// the layout performs.  One more block (grid.x = T + 1) writes the
+// per-expert received counts, the dropped and the invalid counts (dynamic
+// shared memory: that block's staged entries and histogram, or a token
+// block's per-wave rank counts).
 template <int PPT, int MODE, int U, bool LL>
 __global__ void __launch_bounds__(256)
 dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict__ topk_idx, int K,
@@ -339,54 +339,80 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
         write_num_dropped(offsets, E, padded, cap_or_rows, num_dropped);
     }
 
-    const char *xrow = reinterpret_cast<const char *>(x) + (size_t)t * H * 2;
+    // LL: the token's experts (lane k holds expert k) and the first pass of
+    // earlier entries are requested before the row, so that the ranking
+    // below waits for them and not for the row.
+    int ll_e = -1;
+    int ent0[4];
+    if constexpr (LL) {
+        const int row0 = t * K;
+        ll_e = (tid & (kWave - 1)) < K ? topk_idx[row0 + (tid & (kWave - 1))] : -1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = u * bd + tid;
+            ent0[u] = i < row0 + K - 1 ? topk_idx[i] : -1;
+        }
+    }
+
+    // the row through a buffer descriptor: pieces past it read as zero with
+    // no branch, so the loads are issued unconditionally and the waits for
+    // the entries above can leave them in flight
+    const rsrc_t xrow = row_rsrc(reinterpret_cast<const char *>(x) + (size_t)t * H * 2, H * 2);
     u32x4 v[PPT][U];
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
         const int i = seg0 + tid + j * bd;
 #pragma unroll
         for (int h = 0; h < U; ++h)
-            v[j][h] = i < units ? ld16(xrow + ((size_t)i * U + h) * 16) : u32x4{0u, 0u, 0u, 0u};
+            v[j][h] = row_ld16_cached(xrow, (i * U + h) * 16);
     }
 
     // LL: lane k's rank (k < K <= 64), counted while the row is in flight.
-    // For each of the token's experts, every thread compares the earlier
-    // entries at its positions (4 per round, read together), each wave sums
-    // its matches with ballots and popcounts, and adds them to the expert's
-    // counter in shared memory.  The staged entries also give the experts to
-    // the slot loop below, with no second global load.
+    // Each thread holds the entries at its positions in registers (4 per
+    // pass of 4 * blockDim.x entries, one coalesced round trip per pass);
+    // for each of the token's experts every wave counts the matches among
+    // the entries before (t,k) with ballots and popcounts and keeps the
+    // count in lane k; one barrier then adds the waves' counts.  Lane k also
+    // holds expert k of the token for the slot loop below.
     int ll_rank = 0;
     if constexpr (LL) {
-        const int n = (t + 1) * K;
-        int32_t *rk = ll_lds + ((int)gridDim.x - 1) * K;
-        stage_ints(topk_idx, n, ll_lds);
-        if (tid < K)
-            rk[tid] = 0;
-        __syncthreads();
-        const int lane = tid & (kWave - 1);
-        const int ek = lane < K ? ll_lds[t * K + lane] : -1;
-        for (int k = 0; k < K; ++k) {
-            const int e = __builtin_amdgcn_readlane(ek, k);
-            if ((unsigned)e >= (unsigned)E)
-                continue;
-            const int lim = t * K + k;
-            int cnt = 0;
-            for (int i0 = 0; i0 < lim; i0 += 4 * bd) {
-                bool hit[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {          // 4 shared-memory reads in flight
-                    const int i = i0 + u * bd + tid;
-                    hit[u] = ll_lds[i < lim ? i : 0] == e && i < lim;   // lim >= 1
-                }
+        const int lane = tid & (kWave - 1), w = tid / kWave;
+        const int row0 = t * K;
+        int mine = 0;
+        auto count_pass = [&](const int (&ent)[4], int i0) {
+            for (int k = 0; k < K; ++k) {
+                const int e = __builtin_amdgcn_readlane(ll_e, k);
+                if ((unsigned)e >= (unsigned)E)
+                    continue;
+                const int lim = row0 + k;
+                int cnt = 0;
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    cnt += __builtin_popcountll(ballot(hit[u]));
+                    cnt += __builtin_popcountll(ballot(ent[u] == e && i0 + u * bd + tid < lim));
+                mine += lane == k ? cnt : 0;
             }
-            if (lane == 0 && cnt)
-                atomicAdd(&rk[k], cnt);
+        };
+        // a straight-line use of the entries: the wait for them here does not
+        // wait for the row, which the compiler would otherwise flush before
+        // the loop over k
+        asm volatile("" ::"v"(ll_e), "v"(ent0[0]), "v"(ent0[1]), "v"(ent0[2]), "v"(ent0[3]));
+        count_pass(ent0, 0);
+        for (int i0 = 4 * bd; i0 < row0 + K - 1; i0 += 4 * bd) {
+            int ent[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * bd + tid;
+                ent[u] = i < row0 + K - 1 ? topk_idx[i] : -1;
+            }
+            count_pass(ent, i0);
         }
+        int32_t *wcnt = ll_lds;                       // [waves][K]
+        if (lane < K)
+            wcnt[w * K + lane] = mine;
         __syncthreads();
-        ll_rank = lane < K ? rk[lane] : 0;
+        if (lane < K)
+            for (int ww = 0; ww < bd / kWave; ++ww)
+                ll_rank += wcnt[ww * K + lane];
     }
 
     // q: the unit's codes (8U bytes, or 4U for e2m1); sc: its group's scale
@@ -442,7 +468,7 @@ dispatch_kernel(const uint16_t *__restrict__ x, int H, const int32_t *__restrict
         const int k = k0 + lane;
         int sl = -1;
         if (k < K) {
-            const int e = LL ? ll_lds[t * K + k] : trow[k];   // LL: staged with the rest
+            const int e = LL ? ll_e : trow[k];                // LL: k == lane
             if ((unsigned)e < (unsigned)E) {
                 int r;
                 if constexpr (LL) {
@@ -697,8 +723,9 @@ hipError_t launch_ll_dispatch(const uint16_t *x, int T, int H, const int32_t *to
     p.nchunk = 1;
     const bool pairs = pairs_for(quant, H);
     const RowShape rs = ll_shape(quant, H);
-    // the staged entries, the token's rank counters, the count block's histogram
-    const size_t lds = ((size_t)T * K + 64 + E) * sizeof(int32_t);
+    // the count block's staged entries and histogram; the token blocks' rank
+    // counts per wave (4 waves x K)
+    const size_t lds = std::max<size_t>((size_t)T * K + 64 + E, 4 * 64) * sizeof(int32_t);
     EP_MODE_SWITCH(true, p, rs, x, H, topk_idx, nullptr, 1, cap, recv_x, recv_scales, slot,
                    recv_src, num_dropped, nullptr, nullptr, nullptr, recv_count, num_invalid, lds,
                    s);
