@@ -750,8 +750,12 @@ def inputs_sha256(c):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 50; 1000 for the decode and toy workloads, "
+                         "whose steps take microseconds, so that the timed region lasts "
+                         "milliseconds)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: 20; 200 for decode and toy)")
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "toy", "decode", "expert_choice", "large_padded", "expert_choice_tc"])
     ap.add_argument("--quant", default=None, choices=sorted(QUANT_MODES),
@@ -781,6 +785,11 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the multi-GPU "
               "exchange is not built", file=sys.stderr)
         sys.exit(2)
+    short = a.workload in ("decode", "toy")
+    if a.steps is None:
+        a.steps = 1000 if short else 50
+    if a.warmup is None:
+        a.warmup = 200 if short else 20
 
     import torch
     import combine_get_dispatch_04_amd._native as N
