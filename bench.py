@@ -524,12 +524,14 @@ def snapshot(path, torch):
 
 def _combine_bad(got_bits, ref_bits):
     """Elements outside |gpu - oracle| <= 2^-7 |oracle| + 1e-3 (fp32-widened
-    bf16); a NaN or infinity on either side counts as outside."""
+    bf16); a NaN or infinity on either side counts as outside (against an
+    infinite oracle value the bound itself would be infinite)."""
     f = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32) \
         .astype(np.float64)
     g, r = f(got_bits), f(ref_bits)
     with np.errstate(invalid="ignore", over="ignore"):
-        return int(np.count_nonzero(~(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-3)))
+        ok = np.isfinite(g) & np.isfinite(r) & (np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-3)
+    return int(np.count_nonzero(~ok))
 
 
 def _combine_bad_f32(got, ref):
@@ -537,7 +539,8 @@ def _combine_bad_f32(got, ref):
     g = np.asarray(got, np.float32).astype(np.float64)
     r = np.asarray(ref, np.float32).astype(np.float64)
     with np.errstate(invalid="ignore", over="ignore"):
-        return int(np.count_nonzero(~(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-3)))
+        ok = np.isfinite(g) & np.isfinite(r) & (np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-3)
+    return int(np.count_nonzero(~ok))
 
 
 class _Checks:

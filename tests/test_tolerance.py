@@ -29,14 +29,19 @@ def test_non_finite_result_fails(planted, where):
     assert T.combine_bad(got, REF)[0].tolist() == [where]
 
 
-@pytest.mark.parametrize("planted", [0x7FC0, 0x7F80])
+@pytest.mark.parametrize("planted", [0x7FC0, 0x7F80, 0xFF80])
 def test_non_finite_oracle_fails(planted):
     """An oracle value that is not finite (out of contract) never passes,
-    even against the same bits."""
+    even against the same bits, and not against any finite value either
+    (where |oracle| = inf would make the bound itself infinite)."""
     ref = REF.copy()
     ref[1] = planted
     with pytest.raises(AssertionError):
         T.assert_combine_close(ref.copy(), ref)
+    for finite in (0x0000, 0x3F80, 0x7F7F, 0xFF7F):      # 0, 1, +-largest finite
+        got = ref.copy()
+        got[1] = finite
+        assert T.combine_bad(got, ref)[0].tolist() == [1], hex(finite)
 
 
 def test_equal_passes_and_2d():
@@ -72,6 +77,9 @@ def test_f32_non_finite_fails(planted):
         got[where] = planted
         with pytest.raises(AssertionError):
             T.assert_f32_close(got, ref)
+        # the non-finite value on the oracle side, against finite results
+        with pytest.raises(AssertionError):
+            T.assert_f32_close(ref.copy(), got)
 
 
 def test_f32_bound_edges():

@@ -2,10 +2,11 @@
 
     |gpu - oracle| <= 2^-7 * |oracle| + 1e-3
 
-An element passes only when that comparison is TRUE, so a NaN on either side
-(whose difference is NaN, and NaN <= anything is false) or an infinity
-(inf - finite = inf, inf - inf = NaN) fails it.  numpy only: the check
-itself is tested on the CPU.
+An element passes only when both values are finite and that comparison is
+true.  A NaN on either side fails (NaN <= anything is false), and so does an
+infinity on either side: an infinite oracle value is out of contract, and
+against it the bound itself would be infinite.  numpy only: the check itself
+is tested on the CPU.
 """
 import numpy as np
 
@@ -24,7 +25,7 @@ def combine_bad(got_bits, ref_bits):
     if g.shape != r.shape:
         raise AssertionError(f"shape {g.shape} against {r.shape}")
     with np.errstate(invalid="ignore", over="ignore"):
-        ok = np.abs(g - r) <= REL * np.abs(r) + ABS
+        ok = np.isfinite(g) & np.isfinite(r) & (np.abs(g - r) <= REL * np.abs(r) + ABS)
     return np.nonzero(~ok)
 
 
@@ -44,7 +45,7 @@ def f32_bad(got, ref):
     if g.shape != r.shape:
         raise AssertionError(f"shape {g.shape} against {r.shape}")
     with np.errstate(invalid="ignore", over="ignore"):
-        ok = np.abs(g - r) <= REL * np.abs(r) + ABS
+        ok = np.isfinite(g) & np.isfinite(r) & (np.abs(g - r) <= REL * np.abs(r) + ABS)
     return np.nonzero(~ok)
 
 
