@@ -199,8 +199,9 @@ def dequantise(torch, recv, scales, quant, H):
 
 def chunked_token_choice_path(c, N, torch, dev, sp, chunk):
     """The same step in rounds of at most `chunk` tokens (long-sequence
-    chunking): each round runs layout, dispatch and combine on its slice of
-    tokens, reusing one receive buffer of chunk*K rows and one workspace."""
+    chunking): one layout call for every round (ep_get_dispatch_layout_rounds),
+    then dispatch and combine round by round on its slice of tokens, reusing
+    one receive buffer of chunk*K rows."""
     T, H, E, K = c.T, c.H, c.E, c.K
     if c.quant != "bf16" or c.layout != "contiguous":
         raise SystemExit("--chunk is measured for the bf16 contiguous layout")
@@ -209,38 +210,43 @@ def chunked_token_choice_path(c, N, torch, dev, sp, chunk):
     idx = torch.from_numpy(c.topk_idx).to(dev)
     w = torch.from_numpy(c.topk_weights).to(dev)
     n_valid = int(((c.topk_idx >= 0) & (c.topk_idx < E)).sum())
-    ws_bytes = N.ep_workspace_bytes(min(chunk, T), K, E, 1)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    tpr = torch.empty(1, dtype=torch.int32, device=dev)
-    itr = torch.empty((min(chunk, T), 1), dtype=torch.uint8, device=dev)
-    ninv = torch.empty(1, dtype=torch.int32, device=dev)
-    rows = min(chunk, T) * K
+    rt = min(chunk, T)
+    nr = (T + rt - 1) // rt
+    ws_all = N.ep_workspace_bytes_rounds(T, K, E, 1, chunk)
+    stride = N.ep_workspace_bytes(rt, K, E, 1)
+    ws = torch.empty(ws_all, dtype=torch.uint8, device=dev)
+    counts = torch.empty((nr, E), dtype=torch.int32, device=dev)
+    offsets = torch.empty((nr, E + 1), dtype=torch.int32, device=dev)
+    tpr = torch.empty((nr, 1), dtype=torch.int32, device=dev)
+    itr = torch.empty((T, 1), dtype=torch.uint8, device=dev)
+    ninv = torch.empty(nr, dtype=torch.int32, device=dev)
+    rows = rt * K
     recv = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
-    slot = torch.empty((min(chunk, T), K), dtype=torch.int32, device=dev)
+    slot = torch.empty((rt, K), dtype=torch.int32, device=dev)
     src = torch.empty(rows, dtype=torch.int32, device=dev)
     nd = torch.empty(1, dtype=torch.int32, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    ops = []
-    for t0 in range(0, T, chunk):
-        t1 = min(T, t0 + chunk)
+
+    def layout():
+        N.ep_get_dispatch_layout_rounds(P(idx), T, K, E, 1, chunk, P(counts), P(offsets), P(tpr),
+                                        P(itr), P(ninv), P(ws), ws_all, sp)
+
+    ops = [("layout", layout)]
+    for r in range(nr):
+        t0, t1 = r * rt, min(T, (r + 1) * rt)
         n = t1 - t0
-        xs, ids, ws_, outs = x[t0:t1], idx[t0:t1], w[t0:t1], out[t0:t1]
+        xs, ids, ws_, outs, offs = x[t0:t1], idx[t0:t1], w[t0:t1], out[t0:t1], offsets[r]
+        wsr, wsr_bytes = ws[stride * r:], N.ep_workspace_bytes(n, K, E, 1)
 
-        def layout(ids=ids, n=n):
-            N.ep_get_dispatch_layout(P(ids), n, K, E, 1, P(counts), P(offsets), P(tpr), P(itr),
-                                     P(ninv), P(ws), ws_bytes, sp)
-
-        def dispatch(xs=xs, ids=ids, n=n):
-            N.ep_dispatch(P(xs), n, H, P(ids), K, E, P(offsets), N.EP_LAYOUT_CONTIGUOUS, n * K,
-                          N.EP_QUANT_BF16, P(recv), None, P(slot), P(src), P(nd), P(ws),
-                          ws_bytes, sp)
+        def dispatch(xs=xs, ids=ids, n=n, offs=offs, wsr=wsr, wsr_bytes=wsr_bytes):
+            N.ep_dispatch(P(xs), n, H, P(ids), K, E, P(offs), N.EP_LAYOUT_CONTIGUOUS, n * K,
+                          N.EP_QUANT_BF16, P(recv), None, P(slot), P(src), P(nd), P(wsr),
+                          wsr_bytes, sp)
 
         def combine(ws_=ws_, outs=outs, n=n):
             N.ep_combine(P(recv), n * K, H, P(slot), P(ws_), n, K, P(outs), sp)
 
-        ops += [("layout", layout), ("dispatch", dispatch), ("combine", combine)]
+        ops += [("dispatch", dispatch), ("combine", combine)]
     alg = {"layout": T * K * 4,
            "dispatch": T * H * 2 + n_valid * 2 * H + 2 * T * K * 4,
            "combine": n_valid * H * 2 + T * H * 2 + 2 * T * K * 4}
@@ -248,10 +254,12 @@ def chunked_token_choice_path(c, N, torch, dev, sp, chunk):
             "combine": "combine_kernel"}
     meta = {"T": T, "H": H, "E": E, "top_k": K, "recv_layout": "contiguous", "quant": "bf16",
             "combine": "weighted", "valid_slots": n_valid, "chunk_tokens": chunk,
-            "rounds": (T + chunk - 1) // chunk, "receive_rows": rows}
+            "rounds": nr, "receive_rows": rows}
     last = (T - 1) // chunk * chunk
     return Path(c.name, T, ops, kern, alg, meta, kind="chunked",
-                outputs={"out": out, "slot": slot[:T - last], "last_round_t0": last})
+                outputs={"out": out, "slot": slot[:T - last], "last_round_t0": last,
+                         "counts": counts, "offsets": offsets, "num_invalid": ninv,
+                         "round_tokens": rt})
 
 
 def token_choice_path(c, N, torch, dev, sp):
@@ -603,13 +611,21 @@ def _check_token_choice(oracle, torch, c, path, g, ck):
 
 def _check_chunked(oracle, c, path, g, ck):
     T, K, E = c.T, c.K, c.E
+    rt = g["round_tokens"]
+    for r in range(g["counts"].shape[0]):                # every round's layout
+        L = oracle.layout(c.topk_idx[r * rt:(r + 1) * rt], E)
+        ck.equal(f"counts (round {r})", g["counts"][r], L["counts"])
+        ck.equal(f"offsets (round {r})", g["offsets"][r], L["offsets"])
+        ck.equal(f"num_invalid (round {r})", g["num_invalid"][r:r + 1],
+                 np.array([L["num_invalid"]], np.int32))
     t0 = g["last_round_t0"]
     s_last, _, _ = oracle.slots(c.topk_idx[t0:], E, False, (T - t0) * K)
     ck.equal("slot (last round)", g["slot"], s_last)
     s_ref, _, _ = oracle.slots(c.topk_idx, E, False, T * K)
     y = oracle.dispatch_bf16(c.x, s_ref, T * K)
     ck.close("combine", g["out"], oracle.combine(y, s_ref, c.topk_weights))
-    return f"chunked: last round's slots, {T} combined tokens against the unchunked oracle"
+    return (f"chunked: every round's layout, the last round's slots, {T} combined tokens "
+            "against the unchunked oracle")
 
 
 def _check_ranks(oracle, c, path, g, ck):

@@ -27,6 +27,9 @@ SIGNATURES = {
     "ep_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "ep_ec_workspace_bytes": (_SZ, [_I, _I, _I]),
     "ep_get_dispatch_layout": (_ST, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "ep_workspace_bytes_rounds": (_SZ, [_I, _I, _I, _I, _I]),
+    "ep_get_dispatch_layout_rounds": (_ST, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ,
+                                            _P]),
     "ep_dispatch": (_ST, [_P, _I, _I, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "ep_low_latency_dispatch": (_ST, [_P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                                       _P, _P]),
@@ -91,6 +94,19 @@ def ep_get_dispatch_layout(topk_idx, T, K, E, R, counts, offsets, tokens_per_ran
     st = lib().ep_get_dispatch_layout(topk_idx, T, K, E, R, counts, offsets, tokens_per_rank,
                                       is_token_in_rank, num_invalid, ws, ws_bytes, stream)
     return _check("ep_get_dispatch_layout", st) if check else st
+
+
+def ep_workspace_bytes_rounds(T: int, K: int, E: int, R: int, round_tokens: int) -> int:
+    return lib().ep_workspace_bytes_rounds(T, K, E, R, round_tokens)
+
+
+def ep_get_dispatch_layout_rounds(topk_idx, T, K, E, R, round_tokens, counts, offsets,
+                                  tokens_per_rank, is_token_in_rank, num_invalid, ws, ws_bytes,
+                                  stream, check=True):
+    st = lib().ep_get_dispatch_layout_rounds(topk_idx, T, K, E, R, round_tokens, counts, offsets,
+                                             tokens_per_rank, is_token_in_rank, num_invalid, ws,
+                                             ws_bytes, stream)
+    return _check("ep_get_dispatch_layout_rounds", st) if check else st
 
 
 def ep_dispatch(x, T, H, topk_idx, K, E, offsets, layout, cap_or_max_rows, quant, recv_x,

@@ -13,7 +13,7 @@ EpError (a ValueError).
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Optional
+from typing import List, Optional
 
 import torch
 
@@ -116,6 +116,44 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int
                                  _ptr(tpr), _ptr(itr), _ptr(ninv), _ptr(ws), ws_bytes,
                                  _stream(dev))
     return Layout(tpr, None, counts, itr, offsets, ninv, topk_idx, E, R, ws)
+
+
+def get_dispatch_layout_rounds(topk_idx: torch.Tensor, num_experts: int, round_tokens: int,
+                               num_ranks: int = 1) -> List[Layout]:
+    """The layouts of rounds of at most `round_tokens` tokens ("DeepSeek-V4
+    昇腾 NPU 推理部署实践", custom_params: moe_chunk_max_len), all from one
+    call: round r's Layout equals get_dispatch_layout(topk_idx[r*rt:(r+1)*rt])
+    and carries its own slice of the shared workspace for that round's
+    dispatch."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    if round_tokens < 1:
+        raise ValueError("round_tokens must be >= 1")
+    T, K = topk_idx.shape
+    E, R = int(num_experts), int(num_ranks)
+    dev = topk_idx.device
+    ws_bytes = N.ep_workspace_bytes_rounds(T, K, E, R, round_tokens)
+    if ws_bytes == 0:
+        raise N.EpError("ep_workspace_bytes_rounds", N.EP_ERR_INVALID_ARG)
+    rt = min(round_tokens, T)
+    nr = (T + rt - 1) // rt if T else 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    counts = torch.empty((max(nr, 1), E), dtype=torch.int32, device=dev)
+    offsets = torch.empty((max(nr, 1), E + 1), dtype=torch.int32, device=dev)
+    tpr = torch.empty((max(nr, 1), R), dtype=torch.int32, device=dev)
+    itr = torch.empty((T, R), dtype=torch.uint8, device=dev)
+    ninv = torch.empty(max(nr, 1), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        N.ep_get_dispatch_layout_rounds(_ptr(topk_idx), T, K, E, R, round_tokens, _ptr(counts),
+                                        _ptr(offsets), _ptr(tpr), _ptr(itr), _ptr(ninv),
+                                        _ptr(ws), ws_bytes, _stream(dev))
+    stride = N.ep_workspace_bytes(rt, K, E, R) if nr else 0
+    out = []
+    for r in range(nr):
+        t0, t1 = r * rt, min(T, (r + 1) * rt)
+        b = N.ep_workspace_bytes(t1 - t0, K, E, R)
+        out.append(Layout(tpr[r], None, counts[r], itr[t0:t1], offsets[r], ninv[r:r + 1],
+                          topk_idx[t0:t1], E, R, ws[stride * r:stride * r + b]))
+    return out
 
 
 # quant name -> (ep_quant_t, receive dtype, H divisor of a receive row,
@@ -285,9 +323,9 @@ def dispatch_combine_chunked(x: torch.Tensor, topk_idx: torch.Tensor, num_expert
     """Long prefill in rounds of at most `chunk` tokens ("DeepSeek-V4 昇腾
     NPU 推理部署实践", custom_params: moe_chunk_max_len bounds the tokens an
     MoE layer handles at once, against running out of memory on long
-    sequences).  Each round runs layout, dispatch, `expert` and combine on
-    its own slice of tokens, so a receive buffer holds chunk*K rows instead of
-    T*K.  `expert(recv, scales, layout) -> y` maps the received rows to the
+    sequences).  One call lays out every round (get_dispatch_layout_rounds);
+    each round then runs dispatch, `expert` and combine on its own slice of
+    tokens, so a receive buffer holds chunk*K rows instead of T*K.  `expert(recv, scales, layout) -> y` maps the received rows to the
     bf16 rows combine reads (default: identity, bf16 only).  Results equal
     the unchunked call: a token's rows and their order do not depend on the
     other tokens of its round.  -> out [T, H], plus the per-round (layout,
@@ -299,11 +337,13 @@ def dispatch_combine_chunked(x: torch.Tensor, topk_idx: torch.Tensor, num_expert
     if expert is None and quant != "bf16":
         raise ValueError("a quantised dispatch needs an expert that returns bf16 rows")
     T = x.shape[0]
+    if topk_idx.shape[0] != T:
+        raise ValueError("x and topk_idx disagree on the number of tokens")
     out = torch.empty_like(x)
     rounds = []
-    for t0 in range(0, T, chunk):
-        t1 = min(T, t0 + chunk)
-        L = get_dispatch_layout(topk_idx[t0:t1], num_experts, num_ranks)
+    for r, L in enumerate(get_dispatch_layout_rounds(topk_idx, num_experts, chunk, num_ranks)):
+        t0 = r * min(chunk, T)
+        t1 = t0 + L.topk_idx.shape[0]
         recv, scales, h = dispatch(x[t0:t1], L, quant=quant)
         y = recv if expert is None else expert(recv, scales, L)
         combine(y, h, None if topk_weights is None else topk_weights[t0:t1], out=out[t0:t1])

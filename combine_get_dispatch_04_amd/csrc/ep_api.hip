@@ -184,6 +184,68 @@ ep_status_t ep_get_dispatch_layout(const int32_t *topk_idx, int T, int K, int E,
                                         static_cast<hipStream_t>(stream)));
 }
 
+size_t ep_workspace_bytes_rounds(int T, int K, int E, int R, int round_tokens)
+{
+    if (check_layout_sizes(T, K, E, R) != EP_OK || round_tokens < 1)
+        return 0;
+    const int rt = round_tokens < T ? round_tokens : T;
+    if (rt == 0)
+        return ep::make_layout_plan(0, K, E, R).bytes;
+    const int full = T / rt, last = T - full * rt;
+    const size_t stride = ep::make_layout_plan(rt, K, E, R).bytes;
+    return stride * (size_t)full + (last ? ep::make_layout_plan(last, K, E, R).bytes : 0);
+}
+
+ep_status_t ep_get_dispatch_layout_rounds(const int32_t *topk_idx, int T, int K, int E, int R,
+                                          int round_tokens, int32_t *counts, int32_t *offsets,
+                                          int32_t *tokens_per_rank, uint8_t *is_token_in_rank,
+                                          int32_t *num_invalid, void *ws, size_t ws_bytes,
+                                          void *stream)
+{
+    ep_status_t st = check_layout_sizes(T, K, E, R);
+    if (st != EP_OK)
+        return st;
+    if (round_tokens < 1)
+        return EP_ERR_INVALID_ARG;
+    if ((T > 0 && !topk_idx) || !counts || !offsets || !num_invalid)
+        return EP_ERR_INVALID_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
+        !aligned(tokens_per_rank, 4) || !aligned(num_invalid, 4))
+        return EP_ERR_INVALID_ARG;
+    if ((st = check_ws(ws, ws_bytes, ep_workspace_bytes_rounds(T, K, E, R, round_tokens))) !=
+        EP_OK)
+        return st;
+    if (T == 0)
+        return EP_OK;                       // no rounds: nothing to write
+    const int rt = round_tokens < T ? round_tokens : T;
+    const int full = T / rt, last = T - full * rt;
+    const ep::LayoutPlan p = ep::make_layout_plan(rt, K, E, R);
+    const size_t stride = p.bytes;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    // the full rounds, at most 65535 per launch pair (grid.y / grid.x)
+    for (int r0 = 0; r0 < full; r0 += 65535) {
+        const int n = full - r0 < 65535 ? full - r0 : 65535;
+        hipError_t e = ep::launch_layout(
+            p, topk_idx + (int64_t)r0 * rt * K, counts + (int64_t)r0 * E,
+            offsets + (int64_t)r0 * (E + 1), tokens_per_rank ? tokens_per_rank + (int64_t)r0 * R : nullptr,
+            is_token_in_rank ? is_token_in_rank + (int64_t)r0 * rt * R : nullptr,
+            num_invalid + r0, w + stride * (size_t)r0, s, n, stride);
+        if (e != hipSuccess)
+            return EP_ERR_HIP;
+    }
+    if (last) {
+        const ep::LayoutPlan pl = ep::make_layout_plan(last, K, E, R);
+        const int64_t t0 = (int64_t)full * rt;
+        return hip_status(ep::launch_layout(
+            pl, topk_idx + t0 * K, counts + (int64_t)full * E, offsets + (int64_t)full * (E + 1),
+            tokens_per_rank ? tokens_per_rank + (int64_t)full * R : nullptr,
+            is_token_in_rank ? is_token_in_rank + t0 * R : nullptr, num_invalid + full,
+            w + stride * (size_t)full, s));
+    }
+    return EP_OK;
+}
+
 ep_status_t ep_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx, int K, int E,
                         const int32_t *offsets, ep_recv_layout_t layout, int cap_or_max_rows,
                         ep_quant_t quant, void *recv_x, void *recv_scales, int32_t *slot,

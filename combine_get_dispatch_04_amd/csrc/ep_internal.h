@@ -44,9 +44,13 @@ struct EcPlan {
 };
 EcPlan make_ec_plan(int T, int E, int C);
 
+// `rounds` > 1: that many rounds of p.T tokens side by side (topk_idx,
+// is_token_in_rank and the per-round outputs consecutive), round r's tables
+// at ws + r * round_bytes (a multiple of 256).
 hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *counts,
                          int32_t *offsets, int32_t *tokens_per_rank, uint8_t *is_token_in_rank,
-                         int32_t *num_invalid, char *ws, hipStream_t s);
+                         int32_t *num_invalid, char *ws, hipStream_t s, int rounds = 1,
+                         size_t round_bytes = 0);
 
 // Quantisation modes; the values are those of ep_quant_t.
 constexpr int kQuantBf16 = 0;

@@ -76,7 +76,7 @@ __device__ void offsets_from_totals(const int32_t *tot, int E, int32_t *offsets,
 // compact (not unrolled) and their state lives in shared memory.
 __global__ void __launch_bounds__(1024)
 layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, int R, int CT,
-                    int CE, int nbits, int epl, int key_experts, int key_div,
+                    int CE, int nbits, int epl, int key_experts, int key_div, int64_t rstride,
                     int32_t *__restrict__ chunk_hist,
                     int32_t *__restrict__ local_rank, int32_t *__restrict__ rank_part,
                     int32_t *__restrict__ inval_part, uint8_t *__restrict__ is_token_in_rank,
@@ -84,6 +84,23 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
                     int32_t *__restrict__ tokens_per_rank, int32_t *__restrict__ num_invalid)
 {
     extern __shared__ int32_t lds[];
+    {
+        // rounds of T tokens side by side (grid.y): round y's entries, its
+        // tables `rstride` ints further into the workspace, and its outputs
+        const int64_t y = blockIdx.y;
+        topk_idx += y * T * K;
+        chunk_hist += y * rstride;
+        local_rank += y * rstride;
+        rank_part += y * rstride;
+        inval_part += y * rstride;
+        counts += y * E;
+        offsets += y * (E + 1);
+        num_invalid += y;
+        if (tokens_per_rank)
+            tokens_per_rank += y * R;
+        if (is_token_in_rank)
+            is_token_in_rank += y * T * R;
+    }
     const int waves = blockDim.x / kWave;
     const int nchunk = gridDim.x;
     const int per_wave = kWave * epl;                  // a power of two
@@ -293,12 +310,24 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
 // are copied back coalesced.  Columns longer than a tile are done in
 // segments with the running sum kept in the column's thread.
 __global__ void __launch_bounds__(1024)
-layout_scan_kernel(int nchunk, int E, int R, int tile_ints, int32_t *__restrict__ chunk_hist,
-                   const int32_t *__restrict__ rank_part, const int32_t *__restrict__ inval_part,
-                   int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                   int32_t *__restrict__ tokens_per_rank, int32_t *__restrict__ num_invalid)
+layout_scan_kernel(int nchunk, int E, int R, int tile_ints, int64_t rstride,
+                   int32_t *__restrict__ chunk_hist, const int32_t *__restrict__ rank_part,
+                   const int32_t *__restrict__ inval_part, int32_t *__restrict__ counts,
+                   int32_t *__restrict__ offsets, int32_t *__restrict__ tokens_per_rank,
+                   int32_t *__restrict__ num_invalid)
 {
     extern __shared__ int32_t sm[];
+    {
+        const int64_t y = blockIdx.x;                 // one block per round
+        chunk_hist += y * rstride;
+        rank_part += y * rstride;
+        inval_part += y * rstride;
+        counts += y * E;
+        offsets += y * (E + 1);
+        num_invalid += y;
+        if (tokens_per_rank)
+            tokens_per_rank += y * R;
+    }
     const int tid = threadIdx.x, bd = blockDim.x;
     const int ncol = E + R + 1;
     // a segment of a column holds up to `seg` chunks, seg a power of two so
@@ -476,19 +505,23 @@ RankPlan make_rank_plan(int T, int K, int E, int R)
 
 hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *counts,
                          int32_t *offsets, int32_t *tokens_per_rank, uint8_t *is_token_in_rank,
-                         int32_t *num_invalid, char *ws, hipStream_t s)
+                         int32_t *num_invalid, char *ws, hipStream_t s, int rounds,
+                         size_t round_bytes)
 {
     int32_t *hist = reinterpret_cast<int32_t *>(ws + p.off_hist);
     int32_t *rank = reinterpret_cast<int32_t *>(ws + p.off_rank);
     int32_t *rpart = reinterpret_cast<int32_t *>(ws + p.off_rpart);
     int32_t *ipart = reinterpret_cast<int32_t *>(ws + p.off_ipart);
+    const int64_t rstride = (int64_t)(round_bytes / sizeof(int32_t));
     if ((p.CE > 0 ? (long long)p.CE : (long long)p.CT * p.K) > (long long)p.waves * kWave * p.epl)
         return hipErrorInvalidValue;     // a chunk's entries must fit its waves
+    if (rounds < 1 || rounds > 65535 || (rounds > 1 && round_bytes % 256 != 0))
+        return hipErrorInvalidValue;
     if (p.nchunk > 0) {
-        hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunk), dim3(p.waves * kWave), p.lds, s,
-                           topk_idx, p.T, p.K, p.E, p.R, p.CT, p.CE, p.nbits, p.epl,
-                           p.key_experts, p.key_div, hist, rank, rpart, ipart, is_token_in_rank,
-                           counts, offsets, tokens_per_rank, num_invalid);
+        hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunk, rounds), dim3(p.waves * kWave),
+                           p.lds, s, topk_idx, p.T, p.K, p.E, p.R, p.CT, p.CE, p.nbits, p.epl,
+                           p.key_experts, p.key_div, rstride, hist, rank, rpart, ipart,
+                           is_token_in_rank, counts, offsets, tokens_per_rank, num_invalid);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess)
             return err;
@@ -510,9 +543,9 @@ hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *
             if (err != hipSuccess)
                 return err;
         }
-        hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(1024), dyn, s, p.nchunk, p.E, p.R,
-                           tile, hist, rpart, ipart, counts, offsets, tokens_per_rank,
-                           num_invalid);
+        hipLaunchKernelGGL(layout_scan_kernel, dim3(rounds), dim3(1024), dyn, s, p.nchunk, p.E,
+                           p.R, tile, rstride, hist, rpart, ipart, counts, offsets,
+                           tokens_per_rank, num_invalid);
         return hipGetLastError();
     }
     return hipSuccess;

@@ -119,6 +119,36 @@ ep_status_t ep_get_dispatch_layout(const int32_t *topk_idx, int T, int K, int E,
                                    void *stream);
 
 /*
+ * ep_get_dispatch_layout_rounds -- the layout of a long prefill cut into
+ * rounds of at most `round_tokens` tokens ([V4] custom_params:
+ * moe_chunk_max_len, the token count of one MoE round), every round at once:
+ * two launches in all instead of two per round.  Round r covers tokens
+ * [r*round_tokens, min(T, (r+1)*round_tokens)); nr = ceil(T / round_tokens)
+ * rounds.  Each round's outputs equal those of ep_get_dispatch_layout on
+ * that round's rows of topk_idx alone, laid out round after round:
+ *   counts            [nr, E] int32 out.
+ *   offsets           [nr, E+1] int32 out (round-local: each starts at 0).
+ *   tokens_per_rank   [nr, R] int32 out or NULL.
+ *   is_token_in_rank  [T, R] uint8 out or NULL (token rows, as one call).
+ *   num_invalid       [nr] int32 out.
+ *   ws, ws_bytes      >= ep_workspace_bytes_rounds(T, K, E, R, round_tokens).
+ *                     Round r's tables start S*r bytes into ws, where
+ *                     S = ep_workspace_bytes(round_tokens, K, E, R); the
+ *                     round's ep_dispatch takes that slice (ws + S*r, and
+ *                     ws_bytes = ep_workspace_bytes(T_r, K, E, R) for the
+ *                     round's T_r tokens), with x, topk_idx and offsets of
+ *                     the round, on the same stream.
+ * Constraints: those of ep_get_dispatch_layout, and round_tokens >= 1.
+ * Errors as ep_get_dispatch_layout.
+ */
+size_t ep_workspace_bytes_rounds(int T, int K, int E, int R, int round_tokens);
+ep_status_t ep_get_dispatch_layout_rounds(const int32_t *topk_idx, int T, int K, int E, int R,
+                                          int round_tokens, int32_t *counts, int32_t *offsets,
+                                          int32_t *tokens_per_rank, uint8_t *is_token_in_rank,
+                                          int32_t *num_invalid, void *ws, size_t ws_bytes,
+                                          void *stream);
+
+/*
  * ep_dispatch -- [EPA] API Overview, dispatch (contiguous receive buffer)
  * and low_latency_dispatch (per-expert capacity); [EPA] Quantization Modes
  * in Normal Dispatch (bf16; INT8 dynamic and scalar FP8 per token with

@@ -102,6 +102,49 @@ def test_layout_rejects(kw, status):
     assert _layout(**kw) == status
 
 
+def _layout_rounds(**kw):
+    args = dict(topk_idx=A, T=16, K=2, E=8, R=1, round_tokens=4, counts=A, offsets=A,
+                tokens_per_rank=A, is_token_in_rank=A, num_invalid=A, ws=WS, ws_bytes=1 << 20,
+                stream=None)
+    args.update(kw)
+    return N.ep_get_dispatch_layout_rounds(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(round_tokens=0), N.EP_ERR_INVALID_ARG),
+    (dict(round_tokens=-3), N.EP_ERR_INVALID_ARG),
+    (dict(K=0), N.EP_ERR_INVALID_ARG),
+    (dict(T=-1), N.EP_ERR_INVALID_ARG),
+    (dict(E=4097), N.EP_ERR_UNSUPPORTED),
+    (dict(E=8, R=3), N.EP_ERR_INVALID_ARG),
+    (dict(counts=None), N.EP_ERR_INVALID_ARG),
+    (dict(offsets=None), N.EP_ERR_INVALID_ARG),
+    (dict(num_invalid=None), N.EP_ERR_INVALID_ARG),
+    (dict(topk_idx=None), N.EP_ERR_INVALID_ARG),
+    (dict(tokens_per_rank=A + 2), N.EP_ERR_INVALID_ARG),
+    (dict(ws=None), N.EP_ERR_WORKSPACE),
+    (dict(ws=WS + 16), N.EP_ERR_WORKSPACE),
+    (dict(ws_bytes=16), N.EP_ERR_WORKSPACE),
+])
+def test_layout_rounds_rejects(kw, status):
+    assert _layout_rounds(**kw) == status
+
+
+def test_layout_rounds_workspace_bytes():
+    """Full rounds of round_tokens, each the single-call workspace, then the
+    shorter last round's; round_tokens >= T is one round."""
+    one = N.ep_workspace_bytes
+    for T, K, E, R, rt in [(4096, 8, 256, 1, 1024), (4100, 8, 256, 8, 1024), (10, 3, 16, 4, 3),
+                           (7, 2, 8, 1, 100), (5, 1, 4, 1, 1), (100000, 8, 64, 1, 3000)]:
+        full, last = divmod(T, min(rt, T))
+        want = full * one(min(rt, T), K, E, R) + (one(last, K, E, R) if last else 0)
+        assert N.ep_workspace_bytes_rounds(T, K, E, R, rt) == want, (T, K, E, R, rt)
+    assert N.ep_workspace_bytes_rounds(0, 8, 256, 1, 64) == one(0, 8, 256, 1)
+    assert N.ep_workspace_bytes_rounds(10, 2, 8, 1, 0) == 0
+    assert N.ep_workspace_bytes_rounds(10, 0, 8, 1, 4) == 0
+    assert N.ep_workspace_bytes_rounds(10, 2, 6, 4, 4) == 0
+
+
 def _dispatch(**kw):
     args = dict(x=A, T=16, H=256, topk_idx=A, K=2, E=8, offsets=A, layout=0, cap_or_max_rows=32,
                 quant=0, recv_x=B, recv_scales=None, slot=A, recv_src=A, num_dropped=A, ws=WS,

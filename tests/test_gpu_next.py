@@ -127,3 +127,65 @@ def test_chunked_prefill():
     s_ref, _, _ = oracle.slots(c.topk_idx, c.E, False, c.T * c.K)
     ref = oracle.combine(oracle.dispatch_bf16(c.x, s_ref, c.T * c.K), s_ref, c.topk_weights)
     G.assert_combine_close(out, ref)
+
+
+@pytest.mark.parametrize("seed,T,K,E,R,rt", [
+    (1, 4096, 8, 256, 8, 1024),        # prefill rounds, several layout chunks each
+    (2, 1000, 6, 64, 4, 333),          # a shorter last round
+    (3, 50, 3, 16, 2, 1),              # one token per round
+    (4, 300, 5, 40, 1, 5000),          # one round
+    (5, 3, 1500, 300, 4, 2),           # rows longer than a layout chunk
+    (6, 70000, 1, 8, 2, 1),            # more rounds than one launch takes
+])
+def test_layout_rounds_equal_per_round_layouts(seed, T, K, E, R, rt):
+    """ep_get_dispatch_layout_rounds: each round's counts, offsets, tokens
+    per rank, token-in-rank rows and invalid count equal one
+    ep_get_dispatch_layout call on that round's rows, and each round's
+    dispatch from its slice of the shared workspace equals the dispatch of
+    that single call."""
+    _announce(f"layout rounds T={T} K={K} E={E} R={R} rt={rt}")
+    c = W.random_token_choice(seed, T, 16, E, K, p_pad=0.1, p_invalid=0.02, p_dup=0.1)
+    idx_d = G.dev(c.topk_idx)
+    Ls = api.get_dispatch_layout_rounds(idx_d, E, rt, R)
+    n = min(rt, T)
+    assert len(Ls) == (T + n - 1) // n
+    x_d = G.dev(c.x)
+    check_dispatch = len(Ls) <= 64
+    if len(Ls) > 1000:
+        # one token per round and K = 1: every round's tables from the host
+        assert n == 1 and K == 1
+        e = c.topk_idx[:, 0].astype(np.int64)
+        ok = (e >= 0) & (e < E)
+        cnt = np.zeros((T, E), np.int32)
+        cnt[np.nonzero(ok)[0], e[ok]] = 1
+        off = np.concatenate([np.zeros((T, 1), np.int32), np.cumsum(cnt, 1, dtype=np.int32)], 1)
+        itr = np.zeros((T, R), np.uint8)
+        itr[np.nonzero(ok)[0], e[ok] // (E // R)] = 1
+        got = lambda f: torch.stack([f(L) for L in Ls]).cpu().numpy()
+        assert np.array_equal(got(lambda L: L.num_tokens_per_expert), cnt)
+        assert np.array_equal(got(lambda L: L.offsets), off)
+        assert np.array_equal(got(lambda L: L.num_tokens_per_rank), itr.astype(np.int32))
+        assert np.array_equal(got(lambda L: L.is_token_in_rank[0]), itr)
+        assert np.array_equal(got(lambda L: L.num_invalid[0]), ((e != -1) & ~ok).astype(np.int32))
+        return
+    for r, L in enumerate(Ls):
+        t0, t1 = r * n, min(T, (r + 1) * n)
+        one = api.get_dispatch_layout(idx_d[t0:t1], E, R)
+        for a, b in [(L.num_tokens_per_expert, one.num_tokens_per_expert),
+                     (L.offsets, one.offsets), (L.num_tokens_per_rank, one.num_tokens_per_rank),
+                     (L.is_token_in_rank, one.is_token_in_rank), (L.num_invalid, one.num_invalid)]:
+            assert torch.equal(a, b), r
+        if check_dispatch:
+            recv, _, h = api.dispatch(x_d[t0:t1], L)
+            recv1, _, h1 = api.dispatch(x_d[t0:t1], one)
+            assert torch.equal(h.slot, h1.slot), r
+            assert torch.equal(h.num_dropped, h1.num_dropped), r
+            keep = (h.slot >= 0).flatten()
+            rows = h.slot.flatten()[keep].long()
+            assert torch.equal(recv.view(torch.int16)[rows], recv1.view(torch.int16)[rows]), r
+    if T <= 5000:
+        # against the oracle, round by round
+        cnt = torch.stack([L.num_tokens_per_expert for L in Ls]).cpu().numpy()
+        for r in range(len(Ls)):
+            ref = oracle.layout(c.topk_idx[r * n:(r + 1) * n], E)
+            assert np.array_equal(cnt[r], ref["counts"]), r
