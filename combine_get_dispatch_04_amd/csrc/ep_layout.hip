@@ -74,6 +74,7 @@ __device__ void offsets_from_totals(const int32_t *tot, int E, int32_t *offsets,
 // token's rank marks are counted by the chunk its row starts in.  The kernels are short-lived and
 // each CU runs them from a cold instruction cache, so the loops are kept
 // compact (not unrolled) and their state lives in shared memory.
+template <bool ROUNDS>
 __global__ void __launch_bounds__(1024)
 layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, int R, int CT,
                     int CE, int nbits, int epl, int key_experts, int key_div, int64_t rstride,
@@ -84,7 +85,7 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
                     int32_t *__restrict__ tokens_per_rank, int32_t *__restrict__ num_invalid)
 {
     extern __shared__ int32_t lds[];
-    {
+    if constexpr (ROUNDS) {
         // rounds of T tokens side by side (grid.y): round y's entries, its
         // tables `rstride` ints further into the workspace, and its outputs
         const int64_t y = blockIdx.y;
@@ -309,6 +310,7 @@ layout_chunk_kernel(const int32_t *__restrict__ topk_idx, int T, int K, int E, i
 // (rows padded by one int against bank conflicts), and the expert columns
 // are copied back coalesced.  Columns longer than a tile are done in
 // segments with the running sum kept in the column's thread.
+template <bool ROUNDS>
 __global__ void __launch_bounds__(1024)
 layout_scan_kernel(int nchunk, int E, int R, int tile_ints, int64_t rstride,
                    int32_t *__restrict__ chunk_hist, const int32_t *__restrict__ rank_part,
@@ -317,7 +319,7 @@ layout_scan_kernel(int nchunk, int E, int R, int tile_ints, int64_t rstride,
                    int32_t *__restrict__ num_invalid)
 {
     extern __shared__ int32_t sm[];
-    {
+    if constexpr (ROUNDS) {
         const int64_t y = blockIdx.x;                 // one block per round
         chunk_hist += y * rstride;
         rank_part += y * rstride;
@@ -517,8 +519,11 @@ hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *
         return hipErrorInvalidValue;     // a chunk's entries must fit its waves
     if (rounds < 1 || rounds > 65535 || (rounds > 1 && round_bytes % 256 != 0))
         return hipErrorInvalidValue;
+    // the single-call form gets kernels without the round offsets
+    auto chunk_kernel = rounds > 1 ? layout_chunk_kernel<true> : layout_chunk_kernel<false>;
+    auto scan_kernel = rounds > 1 ? layout_scan_kernel<true> : layout_scan_kernel<false>;
     if (p.nchunk > 0) {
-        hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunk, rounds), dim3(p.waves * kWave),
+        hipLaunchKernelGGL(chunk_kernel, dim3(p.nchunk, rounds), dim3(p.waves * kWave),
                            p.lds, s, topk_idx, p.T, p.K, p.E, p.R, p.CT, p.CE, p.nbits, p.epl,
                            p.key_experts, p.key_div, rstride, hist, rank, rpart, ipart,
                            is_token_in_rank, counts, offsets, tokens_per_rank, num_invalid);
@@ -537,13 +542,13 @@ hipError_t launch_layout(const LayoutPlan &p, const int32_t *topk_idx, int32_t *
         const int tile = (int)std::max<long long>(kScanTileInts, std::min(want, room));
         const size_t dyn = (size_t)(tile + p.E + 32) * sizeof(int32_t);
         if (dyn > 65536) {
-            hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(layout_scan_kernel),
+            hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(scan_kernel),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  (int)dyn);
             if (err != hipSuccess)
                 return err;
         }
-        hipLaunchKernelGGL(layout_scan_kernel, dim3(rounds), dim3(1024), dyn, s, p.nchunk, p.E,
+        hipLaunchKernelGGL(scan_kernel, dim3(rounds), dim3(1024), dyn, s, p.nchunk, p.E,
                            p.R, tile, rstride, hist, rpart, ipart, counts, offsets,
                            tokens_per_rank, num_invalid);
         return hipGetLastError();
