@@ -18,7 +18,9 @@
 //   combine): the pack's rows grouped by rank in token order with the local
 //   ids, the receiver's scatter, partial sums, and the sum over ranks giving
 //   bf16(m_t * x_t) exactly with unit weights;
-//   the no-allocation layout + dispatch: the same slots and rows as the pair.
+//   the no-allocation layout + dispatch: the same slots and rows as the pair;
+//   the layouts of every round of a chunked prefill from one call, each
+//   round dispatched from its slice of the workspace.
 // Exit status 0 = every check passed.  Built by tests/capi/build.py.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -26,6 +28,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "ep.h"
@@ -442,6 +445,99 @@ static int rank_share()
     return 0;
 }
 
+// Rounds of a chunked prefill ([V4] custom_params, moe_chunk_max_len): one
+// ep_get_dispatch_layout_rounds call, then each round's dispatch from its
+// slice of the workspace; every round's counts, offsets and slots equal a
+// single layout + dispatch on that round's rows, and the rows arrive.
+static int rounds()
+{
+    const int T = 2500, H = 128, E = 48, K = 5, R = 4, RT = 700;
+    const int NR = (T + RT - 1) / RT;
+    const int64_t TK = (int64_t)T * K;
+    std::vector<int32_t> idx(TK);
+    for (auto &v : idx)
+        v = rnd() % 12 == 0 ? -1 : (int32_t)(rnd() % E);
+    std::vector<uint16_t> x((size_t)T * H);
+    for (size_t i = 0; i < x.size(); ++i)
+        x[i] = (uint16_t)(0x3C00 | (i & 0x3FF));
+    const size_t wsb = ep_workspace_bytes_rounds(T, K, E, R, RT);
+    const size_t S = ep_workspace_bytes(RT, K, E, R);
+    expect(wsb > 0 && S > 0, "rounds: workspace sizes", 0);
+    int32_t *d_idx, *d_cnt, *d_off, *d_tpr, *d_ninv, *d_cnt1, *d_off1, *d_tpr1, *d_ninv1;
+    int32_t *d_slot, *d_slot1, *d_nd;
+    uint16_t *d_x, *d_recv;
+    void *d_ws, *d_ws1;
+    HIP_OK(hipMalloc(&d_idx, TK * 4));
+    HIP_OK(hipMalloc(&d_x, (size_t)T * H * 2));
+    HIP_OK(hipMalloc(&d_cnt, (size_t)NR * E * 4));
+    HIP_OK(hipMalloc(&d_off, (size_t)NR * (E + 1) * 4));
+    HIP_OK(hipMalloc(&d_tpr, (size_t)NR * R * 4));
+    HIP_OK(hipMalloc(&d_ninv, (size_t)NR * 4));
+    HIP_OK(hipMalloc(&d_cnt1, E * 4));
+    HIP_OK(hipMalloc(&d_off1, (E + 1) * 4));
+    HIP_OK(hipMalloc(&d_tpr1, R * 4));
+    HIP_OK(hipMalloc(&d_ninv1, 4));
+    HIP_OK(hipMalloc(&d_slot, (size_t)RT * K * 4));
+    HIP_OK(hipMalloc(&d_slot1, (size_t)RT * K * 4));
+    HIP_OK(hipMalloc(&d_nd, 4));
+    HIP_OK(hipMalloc(&d_recv, (size_t)RT * K * H * 2));
+    HIP_OK(hipMalloc(&d_ws, wsb));
+    HIP_OK(hipMalloc(&d_ws1, S));
+    HIP_OK(hipMemcpy(d_idx, idx.data(), TK * 4, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(d_x, x.data(), (size_t)T * H * 2, hipMemcpyHostToDevice));
+    EP_OK_(ep_get_dispatch_layout_rounds(d_idx, T, K, E, R, RT, d_cnt, d_off, d_tpr, nullptr,
+                                         d_ninv, d_ws, wsb, nullptr));
+    HIP_OK(hipDeviceSynchronize());
+    std::vector<int32_t> cnt((size_t)NR * E), off((size_t)NR * (E + 1)), tpr((size_t)NR * R),
+        ninv(NR);
+    HIP_OK(hipMemcpy(cnt.data(), d_cnt, cnt.size() * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(off.data(), d_off, off.size() * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(tpr.data(), d_tpr, tpr.size() * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(ninv.data(), d_ninv, ninv.size() * 4, hipMemcpyDeviceToHost));
+    for (int r = 0; r < NR; ++r) {
+        const int t0 = r * RT, n = (T - t0 < RT ? T - t0 : RT);
+        const size_t wr = ep_workspace_bytes(n, K, E, R);
+        // the round's slots from the shared workspace
+        EP_OK_(ep_dispatch(d_x + (size_t)t0 * H, n, H, d_idx + (int64_t)t0 * K, K, E,
+                           d_off + (size_t)r * (E + 1), EP_LAYOUT_CONTIGUOUS, n * K,
+                           EP_QUANT_BF16, d_recv, nullptr, d_slot, nullptr, d_nd,
+                           static_cast<char *>(d_ws) + S * r, wr, nullptr));
+        // a single layout + dispatch of the same rows
+        EP_OK_(ep_get_dispatch_layout(d_idx + (int64_t)t0 * K, n, K, E, R, d_cnt1, d_off1,
+                                      d_tpr1, nullptr, d_ninv1, d_ws1, S, nullptr));
+        EP_OK_(ep_dispatch(d_x + (size_t)t0 * H, n, H, d_idx + (int64_t)t0 * K, K, E, d_off1,
+                           EP_LAYOUT_CONTIGUOUS, n * K, EP_QUANT_BF16, d_recv, nullptr, d_slot1,
+                           nullptr, d_nd, d_ws1, S, nullptr));
+        HIP_OK(hipDeviceSynchronize());
+        std::vector<int32_t> c1(E), o1(E + 1), p1(R), s0((size_t)n * K), s1((size_t)n * K);
+        int32_t i1;
+        HIP_OK(hipMemcpy(c1.data(), d_cnt1, E * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(o1.data(), d_off1, (E + 1) * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(p1.data(), d_tpr1, R * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(&i1, d_ninv1, 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(s0.data(), d_slot, s0.size() * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(s1.data(), d_slot1, s1.size() * 4, hipMemcpyDeviceToHost));
+        expect(std::equal(c1.begin(), c1.end(), cnt.begin() + (size_t)r * E), "rounds: counts", r);
+        expect(std::equal(o1.begin(), o1.end(), off.begin() + (size_t)r * (E + 1)),
+               "rounds: offsets", r);
+        expect(std::equal(p1.begin(), p1.end(), tpr.begin() + (size_t)r * R),
+               "rounds: tokens per rank", r);
+        expect(i1 == ninv[r], "rounds: invalid count", r);
+        expect(s0 == s1, "rounds: slots from the round's workspace slice", r);
+        // the counts against the host
+        std::vector<int32_t> hc(E, 0);
+        for (int64_t i = (int64_t)t0 * K; i < (int64_t)(t0 + n) * K; ++i)
+            if (idx[i] >= 0 && idx[i] < E)
+                ++hc[idx[i]];
+        expect(hc == c1, "rounds: counts against the host", r);
+    }
+    hipFree(d_idx); hipFree(d_x); hipFree(d_cnt); hipFree(d_off); hipFree(d_tpr);
+    hipFree(d_ninv); hipFree(d_cnt1); hipFree(d_off1); hipFree(d_tpr1); hipFree(d_ninv1);
+    hipFree(d_slot); hipFree(d_slot1); hipFree(d_nd); hipFree(d_recv); hipFree(d_ws);
+    hipFree(d_ws1);
+    return 0;
+}
+
 // The no-allocation call against the pair on the same input (with a
 // caller workspace): identical counts, offsets, slots and rows.
 static int no_alloc()
@@ -511,7 +607,8 @@ int main()
         fprintf(stderr, "no GPU\n");
         return 2;
     }
-    if (token_choice() || low_latency() || expert_choice() || rank_share() || no_alloc())
+    if (token_choice() || low_latency() || expert_choice() || rank_share() || no_alloc() ||
+        rounds())
         return 2;
     if (failures) {
         fprintf(stderr, "%d check(s) failed\n", failures);

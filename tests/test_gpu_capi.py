@@ -4,7 +4,9 @@ on the host by properties that hold at any size (counts and offsets, the
 slot bijection and its order, received rows equal to their source rows, and
 the exact unit-weight round trip bf16(m_t * x_t)), for token choice, the
 one-launch low-latency dispatch, expert choice and one rank's share of the
-exchange; and the no-allocation call equal to the pair.  No Python between
+exchange; the no-allocation call equal to the pair; and every round's layout
+of a chunked prefill from one call, each round dispatched from its slice of
+the workspace.  No Python between
 the caller and libep."""
 import os
 import subprocess
