@@ -228,13 +228,15 @@ partial_kernel(const uint16_t *__restrict__ y, int y_rows, int H,
             }
         }
     }
-    float *dst = out + (size_t)t * H;
+    // sc1 stores, as for the bf16 rows: the rank share's step (R = 8) went
+    // from 576.6-578.0 to 568.8-569.6 us, this kernel 194.0-194.3 -> 188.3-188.6
+    const rsrc_t dst = row_rsrc(out + (size_t)t * H, units * 16);
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
         const int i = seg0 + threadIdx.x + j * blockDim.x;
         if (i < units)
-            st16(dst + (size_t)i * 4, u32x4{__float_as_uint(acc[j][0]), __float_as_uint(acc[j][1]),
-                                            __float_as_uint(acc[j][2]), __float_as_uint(acc[j][3])});
+            row_st16(dst, i * 16, u32x4{__float_as_uint(acc[j][0]), __float_as_uint(acc[j][1]),
+                                        __float_as_uint(acc[j][2]), __float_as_uint(acc[j][3])});
     }
 }
 
