@@ -699,7 +699,18 @@ hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const 
     // per-token fp8 166.7 -> 155.1, int8 166.5 -> 154.9, MXFP8 170.3 ->
     // 157.3 / 170.0 -> 157.3; MXFP4 (125 MB) 130.7 -> 133.0, bf16 (470 MB)
     // 182.6 -> 183.4, decode with the pair (T = 128) no gain: cached there.
-    const int x_nt = quant != kQuantBf16 && quant != kQuantMxE2M1 && p.T >= 1024;
+    // bf16 rows from a large source (a receiving rank's packed rows: 341 MB
+    // at prefill with 8 ranks) are read non-temporally too while the rows
+    // written stay within a few MALL sizes.  The rank share's step at
+    // prefill: R = 8 571.7-571.9 -> 563.5 us, R = 32 641.5 -> 629.9; with
+    // rows far beyond the MALL (3.4 GB or more: the large workload, alone
+    // or as one rank's share) the default policy was 2-10 us faster.
+    const size_t x_bytes = (size_t)p.T * H * 2;
+    const size_t rows_bytes =
+        (size_t)(padded ? (int64_t)p.E * cap_or_rows : (int64_t)cap_or_rows) * H * 2;
+    const int x_nt = (quant != kQuantBf16 && quant != kQuantMxE2M1 && p.T >= 1024) ||
+                     (quant == kQuantBf16 && x_bytes > ((size_t)128 << 20) &&
+                      rows_bytes <= ((size_t)1 << 30));
     EP_MODE_SWITCH(false, p, rs, x, H, topk_idx, offsets, (int)padded, cap_or_rows, recv_x,
                    recv_scales, slot, recv_src, num_dropped, hist, rank, tamax, nullptr, nullptr,
                    0, x_nt, s);
