@@ -632,14 +632,30 @@ bool pairs_for(int quant, int H)
 // one block (nseg = 0: too long).  Measured at decode (T = 128, H = 7168):
 // bf16 rows (896 units) over 7 one-wave blocks took 13.4 us for the
 // dispatch (events), over 2 blocks of 256 threads 10.3 us.
-RowShape ll_shape(int quant, int H)
+// The low-latency launch: 256 threads per block and, outside the per-token
+// modes, one unit per thread while the token blocks stay within one per CU
+// (256 on MI355X), else two.  At decode (T = 128, H = 7168) the fp8 and
+// MXFP8 codes then take two blocks per token instead of one, which halves
+// each block's encode and store issue (one wave per SIMD: the work is a
+// dependent instruction chain, not bandwidth): step 9.9-10.2 -> 9.5-10.0 us
+// (fp8, 128-channel scales; means of five runs 10.08 -> 9.71), 9.8-10.0 ->
+// 9.3-9.9 (MXFP8).  bf16 with four blocks per token (512 in all) was slower,
+// 12.0 -> 14.4 us, and keeps two units.
+constexpr int64_t kLlBlocks = 256;
+
+RowShape ll_shape(int quant, int H, int T)
 {
     const int units = pairs_for(quant, H) ? H / 16 : H / 8;
-    const int ppt = units <= 256 ? 1 : 2;
-    const int nseg = (units + 2 * 256 - 1) / (2 * 256);
-    if (is_token_mode(quant) && nseg != 1)
-        return {256, 2, 0};
-    return {256, ppt, nseg};
+    if (is_token_mode(quant)) {
+        // the row's max is a block reduction: the row stays in one block
+        if (units > 2 * 256)
+            return {256, 2, 0};
+        return {256, units <= 256 ? 1 : 2, 1};
+    }
+    const int n1 = (units + 255) / 256;
+    if ((int64_t)T * n1 <= kLlBlocks)
+        return {256, 1, n1};
+    return {256, 2, (units + 511) / 512};
 }
 
 }  // namespace
@@ -718,7 +734,7 @@ hipError_t launch_dispatch(const LayoutPlan &p, const uint16_t *x, int H, const 
 
 bool ll_dispatch_fits(int T, int K, int H, int quant)
 {
-    return (int64_t)T * K <= kLlMaxEntries && K <= kLlMaxTopk && ll_shape(quant, H).nseg > 0;
+    return (int64_t)T * K <= kLlMaxEntries && K <= kLlMaxTopk && ll_shape(quant, H, T).nseg > 0;
 }
 
 hipError_t launch_ll_dispatch(const uint16_t *x, int T, int H, const int32_t *topk_idx, int K,
@@ -742,7 +758,7 @@ hipError_t launch_ll_dispatch(const uint16_t *x, int T, int H, const int32_t *to
     p.CT = T;
     p.nchunk = 1;
     const bool pairs = pairs_for(quant, H);
-    const RowShape rs = ll_shape(quant, H);
+    const RowShape rs = ll_shape(quant, H, T);
     // the count block's staged entries and histogram; the token blocks' rank
     // counts per wave (4 waves x K)
     const size_t lds = std::max<size_t>((size_t)T * K + 64 + E, 4 * 64) * sizeof(int32_t);
