@@ -638,7 +638,7 @@ bool pairs_for(int quant, int H)
 // MXFP8 codes then take two blocks per token instead of one, which halves
 // each block's encode and store issue (one wave per SIMD: the work is a
 // dependent instruction chain, not bandwidth): step 9.9-10.2 -> 9.5-10.0 us
-// (fp8, 128-channel scales; means of five runs 10.08 -> 9.71), 9.8-10.0 ->
+// (fp8, 128-channel scales; means of five runs 10.06 -> 9.72), 9.8-10.0 ->
 // 9.3-9.9 (MXFP8).  bf16 with four blocks per token (512 in all) was slower,
 // 12.0 -> 14.4 us, and keeps two units.
 constexpr int64_t kLlBlocks = 256;
