@@ -110,7 +110,40 @@ def test_low_latency_dispatch_parity(mode, T, H, E, K, cap):
     if not _mode_ok(mode, H):
         pytest.skip(f"{mode} needs another H")
     _announce(f"low latency {mode} T={T} H={H} E={E} K={K} cap={cap}")
-    c = _inputs(T * 31 + H + E + K, T, H, E, K)
+    _check_against_oracle(mode, _inputs(T * 31 + H + E + K, T, H, E, K), E, cap)
+
+
+def _sweep_case(i):
+    """A seeded random shape within the one-launch limits (T*K <= 4096,
+    K <= 64, a per-token row within one block of 256 threads x 2 units)."""
+    rng = np.random.default_rng(11000 + i)
+    mode = list(MODES)[i % len(MODES)]
+    if mode == "fp8_e4m3_g128":
+        H = 128 * int(rng.integers(1, 65))
+    elif mode.startswith("mx"):
+        H = 32 * int(rng.integers(1, 257))
+    else:
+        H = 8 * int(rng.integers(1, 1025))
+        if mode in ("fp8_e4m3_token", "int8_token") and (H // 8) % 2 == 1 and H > 4096:
+            H -= 8                          # 16-channel units: at most 512 of them
+    K = int(rng.integers(1, 65)) if rng.random() < 0.2 else int(rng.integers(1, 13))
+    T = int(rng.integers(1, 4096 // K + 1))
+    T = max(1, min(T, 2_000_000 // H))
+    E = int(rng.integers(1, 300))
+    cap = int(rng.integers(0, max(2, 2 * T * K // E + 3)))
+    cap = min(cap, max(1, (1 << 26) // (E * H)))
+    return mode, T, H, E, K, cap
+
+
+@pytest.mark.parametrize("i", range(140))
+def test_low_latency_dispatch_sweep(i):
+    mode, T, H, E, K, cap = _sweep_case(i)
+    _announce(f"low latency sweep {i}: {mode} T={T} H={H} E={E} K={K} cap={cap}")
+    _check_against_oracle(mode, _inputs(500 + i, T, H, E, K), E, cap)
+
+
+def _check_against_oracle(mode, c, E, cap):
+    T, H = c.x.shape
     x_d, idx_d = G.dev(c.x), G.dev(c.topk_idx)
     _, o = _ll(x_d, idx_d, E, cap, MODES[mode])
     torch.cuda.synchronize()
