@@ -197,6 +197,24 @@ def dequantise(torch, recv, scales, quant, H):
     return v.to(torch.bfloat16)
 
 
+def bind(fn, *args):
+    """An entry point bound to its arguments, with every tensor's address
+    taken once here rather than on each call: a decode step lasts about
+    10 us, and taking some fifteen addresses per step from Python took a
+    noticeable part of the host's time to issue it.  The bound call holds
+    the tensors themselves as well: a tensor that only the call uses must
+    stay allocated while the call exists (the caching allocator would
+    otherwise reuse its memory, or hand it back to the driver when a graph
+    capture empties the cache)."""
+    a = tuple(t.data_ptr() if hasattr(t, "data_ptr") else t for t in args)
+
+    def call():
+        fn(*a)
+
+    call.args = args
+    return call
+
+
 def chunked_token_choice_path(c, N, torch, dev, sp, chunk):
     """The same step in rounds of at most `chunk` tokens (long-sequence
     chunking): one layout call for every round (ep_get_dispatch_layout_rounds),
@@ -205,7 +223,6 @@ def chunked_token_choice_path(c, N, torch, dev, sp, chunk):
     T, H, E, K = c.T, c.H, c.E, c.K
     if c.quant != "bf16" or c.layout != "contiguous":
         raise SystemExit("--chunk is measured for the bf16 contiguous layout")
-    P = lambda t: t.data_ptr() if t is not None else None
     x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
     idx = torch.from_numpy(c.topk_idx).to(dev)
     w = torch.from_numpy(c.topk_weights).to(dev)
@@ -227,9 +244,8 @@ def chunked_token_choice_path(c, N, torch, dev, sp, chunk):
     nd = torch.empty(1, dtype=torch.int32, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
-    def layout():
-        N.ep_get_dispatch_layout_rounds(P(idx), T, K, E, 1, chunk, P(counts), P(offsets), P(tpr),
-                                        P(itr), P(ninv), P(ws), ws_all, sp)
+    layout = bind(N.ep_get_dispatch_layout_rounds, idx, T, K, E, 1, chunk, counts, offsets, tpr,
+                  itr, ninv, ws, ws_all, sp)
 
     ops = [("layout", layout)]
     for r in range(nr):
@@ -238,14 +254,9 @@ def chunked_token_choice_path(c, N, torch, dev, sp, chunk):
         xs, ids, ws_, outs, offs = x[t0:t1], idx[t0:t1], w[t0:t1], out[t0:t1], offsets[r]
         wsr, wsr_bytes = ws[stride * r:], N.ep_workspace_bytes(n, K, E, 1)
 
-        def dispatch(xs=xs, ids=ids, n=n, offs=offs, wsr=wsr, wsr_bytes=wsr_bytes):
-            N.ep_dispatch(P(xs), n, H, P(ids), K, E, P(offs), N.EP_LAYOUT_CONTIGUOUS, n * K,
-                          N.EP_QUANT_BF16, P(recv), None, P(slot), P(src), P(nd), P(wsr),
-                          wsr_bytes, sp)
-
-        def combine(ws_=ws_, outs=outs, n=n):
-            N.ep_combine(P(recv), n * K, H, P(slot), P(ws_), n, K, P(outs), sp)
-
+        dispatch = bind(N.ep_dispatch, xs, n, H, ids, K, E, offs, N.EP_LAYOUT_CONTIGUOUS, n * K,
+                        N.EP_QUANT_BF16, recv, None, slot, src, nd, wsr, wsr_bytes, sp)
+        combine = bind(N.ep_combine, recv, n * K, H, slot, ws_, n, K, outs, sp)
         ops += [("dispatch", dispatch), ("combine", combine)]
     alg = {"layout": T * K * 4,
            "dispatch": T * H * 2 + n_valid * 2 * H + 2 * T * K * 4,
@@ -269,7 +280,6 @@ def token_choice_path(c, N, torch, dev, sp):
     padded = c.layout == "padded"
     cap_or_rows = c.cap if padded else T * K
     rows = E * c.cap if padded else T * K
-    P = lambda t: t.data_ptr() if t is not None else None
     x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
     idx = torch.from_numpy(c.topk_idx).to(dev)
     w = torch.from_numpy(c.topk_weights).to(dev)
@@ -297,13 +307,10 @@ def token_choice_path(c, N, torch, dev, sp):
     qcode = getattr(N, qname)
     lay = N.EP_LAYOUT_PADDED if padded else N.EP_LAYOUT_CONTIGUOUS
 
-    def layout():
-        N.ep_get_dispatch_layout(P(idx), T, K, E, 1, P(counts), P(offsets), P(tpr), P(itr),
-                                 P(ninv), P(ws), ws_bytes, sp)
-
-    def dispatch():
-        N.ep_dispatch(P(x), T, H, P(idx), K, E, P(offsets), lay, cap_or_rows, qcode, P(recv),
-                      P(scales), P(slot), P(src), P(nd), P(ws), ws_bytes, sp)
+    layout = bind(N.ep_get_dispatch_layout, idx, T, K, E, 1, counts, offsets, tpr, itr, ninv,
+                  ws, ws_bytes, sp)
+    dispatch = bind(N.ep_dispatch, x, T, H, idx, K, E, offsets, lay, cap_or_rows, qcode, recv,
+                    scales, slot, src, nd, ws, ws_bytes, sp)
 
     if quant != "bf16":
         # identity expert on the dequantised rows, built once outside the timed region
@@ -315,8 +322,7 @@ def token_choice_path(c, N, torch, dev, sp):
     else:
         y = recv
 
-    def combine():
-        N.ep_combine(P(y), rows, H, P(slot), P(w), T, K, P(out), sp)
+    combine = bind(N.ep_combine, y, rows, H, slot, w, T, K, out, sp)
 
     alg = {"layout": T * K * 4,
            "dispatch": T * H * 2 + n_valid * row_bytes(H) + 2 * T * K * 4,
@@ -340,7 +346,6 @@ def low_latency_path(c, N, torch, dev, sp):
     quant = c.quant
     qname, row_bytes, scale_shape = QUANT_MODES[quant]
     rows = E * cap
-    P = lambda t: t.data_ptr() if t is not None else None
     x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
     idx = torch.from_numpy(c.topk_idx).to(dev)
     w = torch.from_numpy(c.topk_weights).to(dev)
@@ -362,9 +367,8 @@ def low_latency_path(c, N, torch, dev, sp):
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     qcode = getattr(N, qname)
 
-    def dispatch():
-        N.ep_low_latency_dispatch(P(x), T, H, P(idx), K, E, cap, qcode, P(recv), P(scales),
-                                  P(slot), P(src), P(cnt), P(nd), P(ninv), sp)
+    dispatch = bind(N.ep_low_latency_dispatch, x, T, H, idx, K, E, cap, qcode, recv, scales,
+                    slot, src, cnt, nd, ninv, sp)
 
     if quant != "bf16":
         # identity expert on the dequantised rows, built once outside the timed region
@@ -375,8 +379,7 @@ def low_latency_path(c, N, torch, dev, sp):
     else:
         y = recv
 
-    def combine():
-        N.ep_combine(P(y), rows, H, P(slot), P(w), T, K, P(out), sp)
+    combine = bind(N.ep_combine, y, rows, H, slot, w, T, K, out, sp)
 
     alg = {"dispatch": T * H * 2 + n_valid * row_bytes(H) + 2 * T * K * 4 + E * 4,
            "combine": n_valid * H * 2 + T * H * 2 + 2 * T * K * 4}
@@ -403,7 +406,6 @@ def ranks_path(c, N, torch, dev, sp, R):
     if c.quant != "bf16" or E % R:
         raise SystemExit("--ranks needs a bf16 token-choice workload with E % R == 0")
     per = E // R
-    P = lambda t: t.data_ptr() if t is not None else None
     x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
     idx = torch.from_numpy(c.topk_idx).to(dev)
     w = torch.from_numpy(c.topk_weights).to(dev)
@@ -436,25 +438,15 @@ def ranks_path(c, N, torch, dev, sp, R):
     part = torch.empty((S, H), dtype=torch.float32, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
-    def pack():
-        N.ep_pack_by_rank(P(x), T, H, P(idx), P(w), K, E, R, S, P(tpr), P(roff), P(send_x),
-                          P(send_src), P(send_idx), P(send_w), P(pos), P(nd), P(pws), pws_bytes,
-                          sp)
-
-    def layout():
-        N.ep_get_dispatch_layout(P(send_idx), S, K, per, 1, P(counts), P(offsets), P(tpr1),
-                                 P(itr), P(ninv), P(rws), rws_bytes, sp)
-
-    def dispatch():
-        N.ep_dispatch(P(send_x), S, H, P(send_idx), K, per, P(offsets), N.EP_LAYOUT_CONTIGUOUS,
-                      n_valid, N.EP_QUANT_BF16, P(recv), None, P(slot), P(src), P(nd_r), P(rws),
-                      rws_bytes, sp)
-
-    def partial():
-        N.ep_combine_partial(P(recv), n_valid, H, P(slot), P(send_w), S, K, P(part), sp)
-
-    def rank_sum():
-        N.ep_combine_ranks(P(part), S, H, P(pos), T, R, P(out), sp)
+    pack = bind(N.ep_pack_by_rank, x, T, H, idx, w, K, E, R, S, tpr, roff, send_x, send_src,
+                send_idx, send_w, pos, nd, pws, pws_bytes, sp)
+    layout = bind(N.ep_get_dispatch_layout, send_idx, S, K, per, 1, counts, offsets, tpr1, itr,
+                  ninv, rws, rws_bytes, sp)
+    dispatch = bind(N.ep_dispatch, send_x, S, H, send_idx, K, per, offsets,
+                    N.EP_LAYOUT_CONTIGUOUS, n_valid, N.EP_QUANT_BF16, recv, None, slot, src, nd_r,
+                    rws, rws_bytes, sp)
+    partial = bind(N.ep_combine_partial, recv, n_valid, H, slot, send_w, S, K, part, sp)
+    rank_sum = bind(N.ep_combine_ranks, part, S, H, pos, T, R, out, sp)
 
     meta_b = 2 * S * K * 4
     alg = {"pack": T * H * 2 + 2 * T * K * 4 + S * H * 2 + S * 4 + 2 * S * K * 4 + T * R * 4,
@@ -481,7 +473,6 @@ def ranks_path(c, N, torch, dev, sp, R):
 
 def expert_choice_path(c, N, torch, dev, sp):
     T, H, E, C = c.T, c.H, c.E, c.C
-    P = lambda t: t.data_ptr()
     x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
     ti = torch.from_numpy(c.token_indices).to(dev)
     w = torch.from_numpy(c.weights).to(dev)
@@ -496,12 +487,9 @@ def expert_choice_path(c, N, torch, dev, sp):
     valid = flat[(flat >= 0) & (flat < T)]
     n_valid, U = int(valid.size), int(np.unique(valid).size)
 
-    def dispatch():
-        N.ep_dispatch_expert_choice(P(x), T, H, P(ti), E, C, P(recv), P(off), P(ent), P(ninv),
-                                    P(ws), ws_bytes, sp)
-
-    def combine():
-        N.ep_combine_expert_choice(P(recv), P(w), E, C, H, P(off), P(ent), T, P(out), sp)
+    dispatch = bind(N.ep_dispatch_expert_choice, x, T, H, ti, E, C, recv, off, ent, ninv, ws,
+                    ws_bytes, sp)
+    combine = bind(N.ep_combine_expert_choice, recv, w, E, C, H, off, ent, T, out, sp)
 
     alg = {"dispatch": U * H * 2 + n_valid * H * 2 + E * C * 4 + (T + 1) * 4 + n_valid * 4,
            "combine": n_valid * H * 2 + T * H * 2 + E * C * 4 + (T + 1) * 4 + n_valid * 4}
@@ -796,6 +784,10 @@ def main():
                          "outside the step's events (0 = no cold pass)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
+    ap.add_argument("--graph", type=int, default=0, metavar="S",
+                    help="time the steps as replays of one HIP graph holding S steps (captured "
+                         "once on a side stream after the warm-up; --steps must be a multiple "
+                         "of S); the per-operation and cold passes stay eager")
     ap.add_argument("--no-check", action="store_true",
                     help="with --cpu-budget 0: skip the check of the timed outputs against "
                          "the oracle (profiling runs)")
@@ -809,6 +801,10 @@ def main():
         a.steps = 1000 if short else 50
     if a.warmup is None:
         a.warmup = 200 if short else 20
+    if a.graph < 0 or (a.graph and a.steps % a.graph):
+        print(f"--steps ({a.steps}) must be a positive multiple of --graph ({a.graph})",
+              file=sys.stderr)
+        sys.exit(2)
 
     import torch
     import combine_get_dispatch_04_amd._native as N
@@ -816,7 +812,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
+    if a.graph:
+        # a graph is captured on a stream of its own, never the null stream
+        stream = torch.cuda.Stream()
+        torch.cuda.set_stream(stream)
+    else:
+        stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     c = W.WORKLOADS[a.workload]()
     c.default_quant = getattr(c, "quant", None)
@@ -850,6 +851,15 @@ def main():
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
+    graph = None
+    if a.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(a.graph):
+                step()
+        for _ in range(max(1, a.warmup // a.graph)):
+            graph.replay()
+        torch.cuda.synchronize()
 
     # timed region: exactly K steps between two device synchronisations, with
     # no per-operation events inside (an event record costs the stream a few
@@ -858,8 +868,12 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     r0.record(stream)
-    for i in range(a.steps):
-        step()
+    if graph is not None:
+        for i in range(a.steps // a.graph):
+            graph.replay()
+    else:
+        for i in range(a.steps):
+            step()
     r1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / a.steps
@@ -976,6 +990,8 @@ def main():
                                              "event packets' gaps)",
                      "rocprof_avg_us": trace_avg_us(key, path.kernel_of[dom])},
     }
+    res["timed_launch"] = (f"replays of one HIP graph of {a.graph} steps" if a.graph
+                           else "eager: each step's entry points called from Python")
     res["cold"] = cold
     res["inputs_sha256"] = inputs_sha256(c)
     parity = None

@@ -1,4 +1,5 @@
-"""Host logic of bench.py, on the CPU: the one-GPU guard, the configuration
+"""Host logic of bench.py, on the CPU: the one-GPU guard, the --graph check,
+the argument binding of the entry points, the configuration
 keys, the bookkeeping that ties a committed profile to the kernel sources it
 was taken on, and the checks the bench applies to its timed outputs (bit
 for bit, and the NaN-proof combine tolerance)."""
@@ -22,6 +23,51 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+@pytest.mark.parametrize("args", [["--steps", "25", "--graph", "10"], ["--graph", "-1"]])
+def test_graph_steps_must_divide_the_timed_steps(args):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "multiple of --graph" in r.stderr
+    assert r.stdout == ""
+
+
+def test_bind_takes_addresses_once():
+    class Buf:
+        calls = 0
+
+        def data_ptr(self):
+            Buf.calls += 1
+            return 4096
+
+    seen = []
+    f = bench.bind(lambda *a: seen.append(a), Buf(), 7, None, Buf())
+    assert Buf.calls == 2
+    f()
+    f()
+    assert Buf.calls == 2
+    assert seen == [(4096, 7, None, 4096)] * 2
+
+
+def test_bind_keeps_its_tensors_alive():
+    """A buffer that only a bound call uses stays allocated while the call
+    exists: with addresses alone, such a tensor was freed as soon as the
+    step was built."""
+    import gc
+    import weakref
+
+    import torch
+    t = torch.empty(16, dtype=torch.int32)
+    ref = weakref.ref(t)
+    f = bench.bind(lambda *a: None, t, 3)
+    del t
+    gc.collect()
+    assert ref() is not None
+    del f
+    gc.collect()
+    assert ref() is None
 
 
 def test_code_only_drops_comments_and_whitespace_only():
