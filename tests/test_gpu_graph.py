@@ -1,10 +1,10 @@
 """The hot path captured in a HIP graph and replayed.
 
-Layout, dispatch and combine (and the expert-choice and low-latency pairs)
-are recorded once through the torch front end (the C ABI enqueues
-everything on the current stream, allocates nothing and issues no memset),
-then the graph is replayed
-with new inputs copied into its static tensors.  Between replays the same
+Layout, dispatch and combine (and the expert-choice and low-latency pairs,
+and one rank's share of the exchange) are recorded once through the torch
+front end (the C ABI enqueues everything on the current stream, allocates
+nothing and issues no memset), then the graph is replayed with new inputs
+copied into its static tensors.  Between replays the same
 calls run eagerly on the new inputs, with synchronisations, and every replay
 must give the eager results bit for bit.
 """
@@ -173,3 +173,59 @@ def test_low_latency_graph_replays(T, H, E, K, cap, quant):
             assert torch.equal(b(go["scales"][kept]), b(e["scales"][kept])), r
         if e["out"] is not None:
             assert torch.equal(b(go["out"]), b(e["out"])), r
+
+
+# (T, H, E, K, R): one rank's share of the exchange at R = 8 and R = 4
+RANK_GRAPH = [(600, 512, 64, 6, 8), (300, 1024, 32, 8, 4)]
+
+
+@pytest.mark.parametrize("T,H,E,K,R", RANK_GRAPH)
+def test_rank_share_graph_replays(T, H, E, K, R):
+    """pack_by_rank, the receiver's layout + scatter of every packed row,
+    combine_partial and combine_ranks captured as one step.  The routing is
+    fixed (so the packed row count S, sized on the host, is too); x and the
+    weights change on every replay."""
+    c = W.random_token_choice(130, T, H, E, K, p_pad=0.1, p_invalid=0.02)
+    per = E // R
+    ids = c.topk_idx
+    ok = (ids >= 0) & (ids < E)
+    S = int(sum(len(set((row[m] // per).tolist())) for row, m in zip(ids, ok)))
+
+    def step(x, idx, w):
+        pk = api.pack_by_rank(x, idx, E, R, topk_weights=w, max_rows=S)
+        _, recv, _, h = api.receive(pk.send_x, pk.send_idx, per)
+        part = api.combine_partial(recv, h, pk.send_w)
+        out = api.combine_ranks(part, pk)
+        return dict(tpr=pk.num_tokens_per_rank, off=pk.rank_offsets, sx=pk.send_x,
+                    src=pk.send_src, sidx=pk.send_idx, sw=pk.send_w, pos=pk.pack_pos,
+                    nd=pk.num_dropped, slot=h.slot, recv=recv, part=part, out=out)
+
+    x_s, idx_s, w_s = _dev_tc(c)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(x_s, idx_s, w_s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        go = step(x_s, idx_s, w_s)
+    b = lambda t: t.view(torch.uint8)
+    for r in range(REPLAYS):
+        c2 = W.random_token_choice(140 + r, T, H, E, K)
+        x = torch.from_numpy(c2.x.view(np.int16)).cuda().view(torch.bfloat16)
+        w = torch.from_numpy(c2.topk_weights).cuda()
+        x_s.copy_(x)
+        w_s.copy_(w)
+        g.replay()
+        torch.cuda.synchronize()
+        e = step(x, idx_s, w)
+        torch.cuda.synchronize()
+        assert int(e["nd"][0]) == 0, r
+        for k in ("tpr", "off", "src", "sidx", "pos", "nd", "slot"):
+            assert torch.equal(go[k], e[k]), (r, k)
+        for k in ("sx", "sw", "part", "out"):
+            assert torch.equal(b(go[k]), b(e[k])), (r, k)
+        kept = e["slot"][e["slot"] >= 0].long()           # receive rows that were written
+        assert torch.equal(b(go["recv"][kept]), b(e["recv"][kept])), r
