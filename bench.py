@@ -126,6 +126,15 @@ def trace_avg_us(key, kernel):
     return None if k is None else k.get("avg_us")
 
 
+def frac_by_trace(bytes_per_launch, avg_us):
+    """Algorithmic bytes of one launch over the kernel's own duration (the
+    committed trace's average, which has no event gaps in it), as a fraction
+    of 8 TB/s; None without a current trace."""
+    if not avg_us:
+        return None
+    return bytes_per_launch / (avg_us * 1e-6) / 1e9 / PEAK_HBM_GBPS
+
+
 def workload_key(c, meta, chunk, two_call, ranks=0):
     """Name of a bench configuration: the workload, plus the dispatch mode
     when it is not the workload's own, the round size, the decode form and
@@ -988,7 +997,9 @@ def main():
                      "avg_launch_us_source": "HIP events around each launch on the kernels' "
                                              "stream, second pass of K steps (includes the "
                                              "event packets' gaps)",
-                     "rocprof_avg_us": trace_avg_us(key, path.kernel_of[dom])},
+                     "rocprof_avg_us": trace_avg_us(key, path.kernel_of[dom]),
+                     "frac_by_rocprof_avg": frac_by_trace(dom_bytes, trace_avg_us(
+                         key, path.kernel_of[dom]))},
     }
     res["timed_launch"] = (f"replays of one HIP graph of {a.graph} steps" if a.graph
                            else "eager: each step's entry points called from Python")

@@ -201,3 +201,9 @@ def test_checks_record_each_output():
     ck.close("combine nan", np.array([0x7FC0], np.uint16), np.array([0x4000], np.uint16))
     assert ck.done == ["same", "combine"]
     assert ck.failed == ["differs", "shape", "zero sign", "combine nan (1)"]
+
+
+def test_frac_by_trace():
+    assert bench.frac_by_trace(8e12 * 90e-6, 90.0) == pytest.approx(1.0)
+    assert bench.frac_by_trace(528744448, 90.33) == pytest.approx(0.7317, abs=1e-4)
+    assert bench.frac_by_trace(1.0, None) is None
